@@ -1,0 +1,171 @@
+"""Seeded synthetic inputs for draft-token verification.
+
+This module only makes inputs: logits rows, draft tokens, uniforms, d2t maps
+and draft-tree topologies, shaped like the workloads the pages describe.  It
+holds none of the verification arithmetic (no softmax, no top-p, no accept
+rule, no residual); the draft tokens come from a Gumbel-max draw over the
+draft logits (a draft-side sampler, upstream of verification), or, for the
+greedy workloads, from NumPy's argmax as each workload's recipe states.
+
+Every array is host NumPy.  bfloat16 tensors are carried as uint16 bit
+patterns (round-to-nearest-even of the float32 value); `bf16_to_f32` widens
+them exactly.  Uniforms are k / 2**24 with k uniform in [0, 2**24), so the
+float32 value is exact and every consumer sees the same number.
+
+Workloads (sizes are parameters; the defaults are the full sizes):
+  sample_plain   B=1,  gamma=3, V=49152, fp32 target ~N(0, 2^2), draft = target + N(0, 0.5^2),
+                 T=1, no top-p.  The tutorial's generate() defaults aside, the vocabulary
+                 size is the one of the 2.16x blog's SmolLM2 model.
+  sample_topp    B=64, gamma=5, V=151936, bf16 target ~N(0, 3^2) with 1% of the ids of
+                 every row raised by +8, draft = target + N(0, 1^2), T=0.8, top-p 0.9
+                 (the tutorial's generate() defaults).
+  greedy         B=128, gamma=6, V=128256, bf16 ~N(0, 2^2); draft token i equals the row's
+                 argmax with probability 0.7, else a uniform other id (the SSD guide's
+                 temperature-0, k=6 benchmark run).
+  eagle_d2t      B=32, gamma=7, Vt=128256, Vd=32000; d2t = sorted random 32000 target ids;
+                 draft fp32 ~N(0, 2^2); target bf16 = mapped draft + N(0, 1^2), unmapped
+                 ~N(-4, 1^2); the bonus row is built the same way from a fresh draft-like
+                 row; T=1 (the SSD guide's EAGLE3 k=7 run).
+  tree           B=16, N=32 nodes, depth <= 5, <= 8 children, V=49152, bf16 ~N(0, 2^2);
+                 node token = argmax of its parent's row with probability 0.6 (the 2.16x
+                 blog's 32-node, depth-5, top-k-8 tree).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits", "bf16_to_f32", "uniforms", "gumbel_draw",
+    "sample_plain", "sample_topp", "greedy", "eagle_d2t", "tree", "WORKLOADS",
+]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float32, exact."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def uniforms(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniforms in [0, 1) of the form k / 2**24, as float32 (exact)."""
+    return (rng.integers(0, 1 << 24, size=shape, dtype=np.int64).astype(np.float64)
+            / float(1 << 24)).astype(np.float32)
+
+
+def _normal(rng, shape, sigma, mean=0.0):
+    return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)
+            + np.float32(mean))
+
+
+def gumbel_draw(rng: np.random.Generator, logits_f32: np.ndarray, temperature: float) -> np.ndarray:
+    """One draw per row of a [..., V] array by the Gumbel-max trick on logits/T.
+
+    A stand-in for the draft model's own sampler; it is not part of
+    verification.  Rows are drawn one by one to bound memory."""
+    flat = logits_f32.reshape(-1, logits_f32.shape[-1])
+    out = np.empty(flat.shape[0], np.int32)
+    for r in range(flat.shape[0]):
+        g = rng.gumbel(size=flat.shape[1])
+        out[r] = int(np.argmax(flat[r].astype(np.float64) / temperature + g))
+    return out.reshape(logits_f32.shape[:-1])
+
+
+def _other_id(rng, V, avoid):
+    """A uniform id in [0, V) different from `avoid` (element-wise)."""
+    r = rng.integers(0, V - 1, size=np.shape(avoid))
+    return (r + (r >= avoid)).astype(np.int32)
+
+
+def sample_plain(seed: int, B: int = 1, gamma: int = 3, V: int = 49152) -> dict:
+    rng = np.random.default_rng(seed)
+    zt = _normal(rng, (B, gamma + 1, V), 2.0)
+    zd = (zt[:, :gamma] + _normal(rng, (B, gamma, V), 0.5)).astype(np.float32)
+    return dict(kind="sample", target=zt, draft=zd,
+                tokens=gumbel_draw(rng, zd, 1.0) if gamma > 0 else np.zeros((B, 0), np.int32),
+                u_accept=uniforms(rng, (B, gamma)), u_sample=uniforms(rng, (B,)),
+                d2t=None, temperature=1.0, top_p=1.0)
+
+
+def sample_topp(seed: int, B: int = 64, gamma: int = 5, V: int = 151936,
+                spike_frac: float = 0.01, temperature: float = 0.8, top_p: float = 0.9) -> dict:
+    rng = np.random.default_rng(seed)
+    zt = _normal(rng, (B, gamma + 1, V), 3.0)
+    n_spike = max(1, int(round(spike_frac * V)))
+    for b in range(B):
+        for i in range(gamma + 1):
+            zt[b, i, rng.choice(V, n_spike, replace=False)] += np.float32(8.0)
+    zd = (zt[:, :gamma] + _normal(rng, (B, gamma, V), 1.0)).astype(np.float32)
+    tb, db = bf16_bits(zt), bf16_bits(zd)
+    return dict(kind="sample", target=tb, draft=db,
+                tokens=(gumbel_draw(rng, bf16_to_f32(db), temperature) if gamma > 0
+                        else np.zeros((B, 0), np.int32)),
+                u_accept=uniforms(rng, (B, gamma)), u_sample=uniforms(rng, (B,)),
+                d2t=None, temperature=temperature, top_p=top_p)
+
+
+def greedy(seed: int, B: int = 128, gamma: int = 6, V: int = 128256, p_match: float = 0.7) -> dict:
+    rng = np.random.default_rng(seed)
+    zb = bf16_bits(_normal(rng, (B, gamma + 1, V), 2.0))
+    am = np.argmax(bf16_to_f32(zb[:, :gamma]), axis=-1).astype(np.int32)
+    match = rng.random(size=(B, gamma)) < p_match
+    tokens = np.where(match, am, _other_id(rng, V, am)).astype(np.int32)
+    return dict(kind="greedy", target=zb, tokens=tokens)
+
+
+def eagle_d2t(seed: int, B: int = 32, gamma: int = 7, Vt: int = 128256, Vd: int = 32000,
+              temperature: float = 1.0) -> dict:
+    rng = np.random.default_rng(seed)
+    d2t = np.sort(rng.choice(Vt, Vd, replace=False)).astype(np.int32)
+    zd = _normal(rng, (B, gamma, Vd), 2.0)
+    aux = _normal(rng, (B, 1, Vd), 2.0)                 # stands in for a draft row at the bonus position
+    src = np.concatenate([zd, aux], axis=1)
+    zt = _normal(rng, (B, gamma + 1, Vt), 1.0, mean=-4.0)
+    zt[:, :, d2t] = src + _normal(rng, (B, gamma + 1, Vd), 1.0)
+    j = gumbel_draw(rng, zd, temperature) if gamma > 0 else np.zeros((B, 0), np.int32)
+    return dict(kind="sample", target=bf16_bits(zt), draft=zd.astype(np.float32),
+                tokens=d2t[j].astype(np.int32), u_accept=uniforms(rng, (B, gamma)),
+                u_sample=uniforms(rng, (B,)), d2t=d2t, temperature=temperature, top_p=1.0)
+
+
+def tree_topology(rng: np.random.Generator, N: int = 32, max_depth: int = 5, max_children: int = 8):
+    """Random parent array: node 0 is the root; node k picks a parent uniformly
+    among earlier nodes with depth < max_depth and fewer than max_children children."""
+    parents = np.full(N, -1, np.int32)
+    depth = np.zeros(N, np.int32)
+    kids = np.zeros(N, np.int32)
+    for k in range(1, N):
+        ok = np.flatnonzero((depth[:k] < max_depth) & (kids[:k] < max_children))
+        p = int(ok[rng.integers(0, len(ok))])
+        parents[k] = p
+        depth[k] = depth[p] + 1
+        kids[p] += 1
+    return parents
+
+
+def tree(seed: int, B: int = 16, N: int = 32, V: int = 49152, max_depth: int = 5,
+         max_children: int = 8, p_match: float = 0.6) -> dict:
+    rng = np.random.default_rng(seed)
+    zb = bf16_bits(_normal(rng, (B, N, V), 2.0))
+    am = np.argmax(bf16_to_f32(zb), axis=-1).astype(np.int32)      # [B, N]
+    parents = np.stack([tree_topology(rng, N, max_depth, max_children) for _ in range(B)])
+    tokens = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for k in range(1, N):
+            g = am[b, parents[b, k]]
+            tokens[b, k] = g if rng.random() < p_match else _other_id(rng, V, g)
+    return dict(kind="tree", target=zb, tokens=tokens, parents=parents)
+
+
+WORKLOADS = {
+    "sample_plain": sample_plain,
+    "sample_topp": sample_topp,
+    "greedy": greedy,
+    "eagle_d2t": eagle_d2t,
+    "tree": tree,
+}

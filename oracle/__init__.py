@@ -1,0 +1,169 @@
+"""CPU oracle for batched draft-token verification (TEST INFRASTRUCTURE ONLY).
+
+The oracle is the plain float64 statement of what the verification path
+computes, written from the pages (see the header of spec_oracle.c for the
+sources and each function for the passage it follows).  Only the test suite,
+the smoke check and the benchmark's CPU-baseline leg may import this package.
+It shares no code with the GPU library and never imports it.
+
+This module compiles spec_oracle.c with the host C compiler (plain -O2, no
+fast-math) into liboracle.so next to it and wraps the entry points with ctypes
+over NumPy arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FLOAT32, BFLOAT16 = 0, 1
+
+ST_TOKEN_RANGE, ST_NO_MASS, ST_BAD_PARENT = 1, 4, 8
+FL_ACCEPT_EDGE, FL_CDF_EDGE, FL_ZERO_RESID = 1, 2, 4
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle.  Plain C, -O2, IEEE semantics (no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = C.CDLL(_LIB)
+        P = C.c_void_p
+        i32, f64 = C.c_int, C.c_double
+        lib.oracle_verify_sample.argtypes = [P, i32, P, i32, P, P, P, P, i32, i32, i32, i32,
+                                             f64, f64, f64, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_row_dist.argtypes = [P, i32, i32, f64, f64, i32, P, P, P, P]
+        lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, P]
+        lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
+        lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _logits(a):
+    """Raw logits as (contiguous array, dtype code).  bfloat16 arrives as uint16 bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, FLOAT32
+    if a.dtype == np.uint16:
+        return a, BFLOAT16
+    raise TypeError("logits must be float32 or uint16 (bfloat16 bits), got %s" % a.dtype)
+
+
+def verify_sample(target_logits, draft_logits, tokens, u_accept, u_sample, temperature, top_p,
+                  d2t=None, band=1e-5, k_delta=None, nthreads=1):
+    """Sampling verification of a batch.  Returns a dict of NumPy arrays:
+    tokens [B, g+1], accept_len [B], p_tok/q_tok [B, g] (float64), status [B],
+    flags [B] (boundary diagnostics), margin [B, 2g+1, 2] (top-p margins, target
+    rows then draft rows)."""
+    tl, tdt = _logits(target_logits)
+    B, g1, Vt = tl.shape
+    g = g1 - 1
+    if g > 0:
+        dl, ddt = _logits(draft_logits)
+        Vd = dl.shape[2]
+        assert dl.shape[:2] == (B, g)
+    else:
+        dl, ddt, Vd = np.zeros(1, np.float32), FLOAT32, (Vt if d2t is None else len(d2t))
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, g)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(B, g)
+    us = np.ascontiguousarray(u_sample, dtype=np.float32).reshape(B)
+    dm = None if d2t is None else np.ascontiguousarray(d2t, dtype=np.int32)
+    kd = None if k_delta is None else np.ascontiguousarray(k_delta, dtype=np.int8).reshape(B, 2 * g + 1)
+    out = dict(tokens=np.empty((B, g + 1), np.int32), accept_len=np.empty(B, np.int32),
+               p_tok=np.empty((B, g), np.float64), q_tok=np.empty((B, g), np.float64),
+               status=np.empty(B, np.int32), flags=np.empty(B, np.int32),
+               margin=np.empty((B, 2 * g + 1, 2), np.float64))
+    rc = _load().oracle_verify_sample(
+        _ptr(tl), tdt, _ptr(dl), ddt, _ptr(tok), _ptr(dm), _ptr(ua), _ptr(us),
+        B, g, Vt, Vd, float(temperature), float(top_p), float(band), _ptr(kd),
+        _ptr(out["tokens"]), _ptr(out["accept_len"]), _ptr(out["p_tok"]), _ptr(out["q_tok"]),
+        _ptr(out["status"]), _ptr(out["flags"]), _ptr(out["margin"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_verify_sample: bad arguments (code %d)" % rc)
+    return out
+
+
+def row_dist(z, temperature, top_p, k_delta=0):
+    """D1 on one row: returns (p [V] float64, status, k, margin_lo, margin_hi)."""
+    z, dt = _logits(np.asarray(z).reshape(-1))
+    V = z.shape[0]
+    p = np.empty(V, np.float64)
+    k = np.zeros(1, np.int32)
+    lo = np.zeros(1, np.float64)
+    hi = np.zeros(1, np.float64)
+    st = _load().oracle_row_dist(_ptr(z), dt, V, float(temperature), float(top_p), int(k_delta),
+                                 _ptr(p), _ptr(k), _ptr(lo), _ptr(hi))
+    if st < 0:
+        raise ValueError("oracle_row_dist: bad arguments")
+    return p, st, int(k[0]), float(lo[0]), float(hi[0])
+
+
+def chain_from_dists(P, Q, tokens, u_accept, u_sample):
+    """D3-D6 on given distributions P [g+1, V], Q [g, V] (float64)."""
+    P = np.ascontiguousarray(P, dtype=np.float64)
+    g1, V = P.shape
+    g = g1 - 1
+    Q = np.ascontiguousarray(Q if g > 0 else np.zeros((1, V)), dtype=np.float64)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(max(g, 1))
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(max(g, 1))
+    out = np.empty(g + 1, np.int32)
+    n = _load().oracle_chain_from_dists(_ptr(P), _ptr(Q), _ptr(tok), _ptr(ua),
+                                        C.c_float(float(u_sample)), g, V, _ptr(out))
+    if n < 0:
+        raise MemoryError("oracle_chain_from_dists")
+    return n, out
+
+
+def verify_greedy(logits, tokens):
+    """Greedy verification: returns dict(tokens [B, g+1], accept_len [B], status [B])."""
+    lg, dt = _logits(logits)
+    B, g1, V = lg.shape
+    g = g1 - 1
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, g)
+    out = dict(tokens=np.empty((B, g + 1), np.int32), accept_len=np.empty(B, np.int32),
+               status=np.empty(B, np.int32))
+    rc = _load().oracle_verify_greedy(_ptr(lg), dt, _ptr(tok), B, g, V, _ptr(out["tokens"]),
+                                      _ptr(out["accept_len"]), _ptr(out["status"]))
+    if rc != 0:
+        raise ValueError("oracle_verify_greedy: bad arguments")
+    return out
+
+
+def verify_tree_greedy(logits, node_tokens, parents):
+    """Greedy tree verification: returns dict(path [B, N], tokens [B, N], accept_len [B], status [B])."""
+    lg, dt = _logits(logits)
+    B, N, V = lg.shape
+    nt = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    pa = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, N)
+    out = dict(path=np.empty((B, N), np.int32), tokens=np.empty((B, N), np.int32),
+               accept_len=np.empty(B, np.int32), status=np.empty(B, np.int32))
+    rc = _load().oracle_verify_tree_greedy(_ptr(lg), dt, _ptr(nt), _ptr(pa), B, N, V,
+                                           _ptr(out["path"]), _ptr(out["tokens"]),
+                                           _ptr(out["accept_len"]), _ptr(out["status"]))
+    if rc != 0:
+        raise ValueError("oracle_verify_tree_greedy: bad arguments")
+    return out
