@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of batched draft-token verification on one MI355X.
+
+One step = one call of the verification path over one batch of synthetic
+inputs already resident in HBM.  Default workload: sampling verification with
+top-p, B=64, gamma=5, V=151936, bfloat16 logits, T=0.8, top-p 0.9 (the rows
+the headline metric is quoted on).  Inputs rotate over several copies in HBM
+(more than three times the 256 MB Infinity Cache in total) so every step reads
+its logits from HBM, not from the cache.
+
+Prints ONE JSON line: verified vocab rows/s (target + draft rows per second),
+the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
+launch time from HIP events on the launch stream, against 8 TB/s), and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified vocab rows/sec and achieved HBM GB/s (% of peak), 1 MI355X"
+PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (generator kwargs, description)
+    "sample_topp": dict(desc="sampling verify + top-p, B=64 gamma=5 V=151936 bf16, T=0.8 top_p=0.9"),
+    "sample_plain": dict(desc="sampling verify, B=1 gamma=3 V=49152 fp32, T=1, no top-p"),
+    "greedy": dict(desc="greedy verify, B=128 gamma=6 V=128256 bf16"),
+    "eagle_d2t": dict(desc="EAGLE3 d2t sampling verify, B=32 gamma=7 Vt=128256 bf16 Vd=32000 fp32, T=1"),
+    "tree": dict(desc="greedy tree verify, B=16 N=32 V=49152 bf16"),
+}
+
+
+def compulsory_bytes(w) -> int:
+    """Every input byte read once plus every output byte written once."""
+    n = w["target"].nbytes + w["tokens"].nbytes
+    if w["kind"] == "sample":
+        n += w["draft"].nbytes + w["u_accept"].nbytes + w["u_sample"].nbytes
+        if w.get("d2t") is not None:
+            n += w["d2t"].nbytes
+        B, g = w["tokens"].shape
+        n += B * (g + 1) * 4 + B * 4 + 2 * B * g * 4 + B * 4      # tokens, len, p/q, status
+    elif w["kind"] == "greedy":
+        B, g = w["tokens"].shape
+        n += B * (g + 1) * 4 + 2 * B * 4
+    else:
+        B, N = w["tokens"].shape
+        n += w["parents"].nbytes + 2 * B * N * 4 + 2 * B * 4
+    return int(n)
+
+
+def rows_per_step(w) -> int:
+    if w["kind"] == "sample":
+        B, g = w["tokens"].shape
+        return B * (2 * g + 1)
+    return int(w["target"].shape[0] * w["target"].shape[1])
+
+
+def make_inputs(name, seed):
+    from draft_token_verification_07_amd import synth
+    return synth.WORKLOADS[name](seed)
+
+
+def device_sets(w, nrot, dev):
+    """The workload's tensors on the GPU, with nrot distinct copies of the
+    logits (the bulk of the bytes) so consecutive steps read different memory."""
+    import torch
+
+    def t(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a.copy()).to(dev)
+
+    base = dict(target=t(w["target"]), tokens=t(w["tokens"].astype(np.int32)))
+    if w["kind"] == "sample":
+        base.update(draft=t(w["draft"]), u_accept=t(w["u_accept"]), u_sample=t(w["u_sample"]),
+                    d2t=t(w.get("d2t")))
+    if w["kind"] == "tree":
+        base["parents"] = t(w["parents"].astype(np.int32))
+    sets = [base]
+    for _ in range(nrot - 1):
+        c = dict(base)
+        c["target"] = base["target"].clone()
+        if "draft" in base:
+            c["draft"] = base["draft"].clone()
+        sets.append(c)
+    torch.cuda.synchronize()
+    return sets
+
+
+def cpu_baseline(w, max_seqs: int):
+    """Time the oracle as it stands on the first max_seqs sequences, with
+    every host core this process may use."""
+    import oracle
+    oracle.build(force=False)
+    cores = min(len(os.sched_getaffinity(0)), 64)
+    B = w["target"].shape[0]
+    s = min(B, max_seqs)
+    sl = slice(0, s)
+    t0 = time.perf_counter()
+    if w["kind"] == "sample":
+        oracle.verify_sample(w["target"][sl], w["draft"][sl], w["tokens"][sl], w["u_accept"][sl],
+                             w["u_sample"][sl], w["temperature"], w["top_p"], d2t=w.get("d2t"),
+                             nthreads=cores)
+        rows = s * (2 * w["tokens"].shape[1] + 1)
+        used = min(cores, s)
+    elif w["kind"] == "greedy":
+        oracle.verify_greedy(w["target"][sl], w["tokens"][sl])
+        rows = s * w["target"].shape[1]
+        used = 1
+    else:
+        oracle.verify_tree_greedy(w["target"][sl], w["tokens"][sl], w["parents"][sl])
+        rows = s * w["target"].shape[1]
+        used = 1
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="rows/s", cores=used, kind="oracle",
+                sample="first %d of %d sequences of the same workload, %.2f s wall" % (s, B, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sample_topp", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=2002)
+    ap.add_argument("--cold-bytes", type=float, default=1.0e9,
+                    help="total bytes of rotated input copies (> 3x the 256 MB Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=64)
+    ap.add_argument("--queue-ahead-cycles", type=float, default=4e7,
+                    help="GPU sleep queued before the timed steps (lets the host run ahead)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="instead of the benchmark, copy this many bytes device-to-device "
+                         "(a kernel of known traffic, to scale rocprofv3 byte counters)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch from rocprofv3 counters, if present")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this verification path shards by sequence with no "
+              "communication, and only --gpus 1 is run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=5)), flush=True)
+        return
+    import draft_token_verification_07_amd as sv
+    from draft_token_verification_07_amd import binding as bnd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.lib()                                   # fails loudly without the HIP library
+
+    print("[bench] generating %s (seed %d)" % (args.workload, args.seed), file=sys.stderr, flush=True)
+    w = make_inputs(args.workload, args.seed)
+    nbytes = compulsory_bytes(w)
+    nrot = max(1, int(math.ceil(args.cold_bytes / nbytes)))
+
+    sets = device_sets(w, nrot, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # preallocated outputs and one workspace (calls on one stream share it)
+    if w["kind"] == "sample":
+        B, g = w["tokens"].shape
+        Vt = w["target"].shape[2]
+        Vd = w["draft"].shape[2]
+        need = sv.sv_workspace_bytes_sample(B, g, Vt, Vd, w["top_p"])
+        outs = (torch.empty((B, g + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty((B, g), dtype=torch.float32, device=dev), torch.empty((B, g), dtype=torch.float32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+
+        def step(s):
+            sv.spec_verify_sample(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
+                                  w["temperature"], w["top_p"], d2t=s["d2t"], ws=ws, out=outs)
+        kernel = "topp_kernel" if w["top_p"] < 1 else "stats_kernel"
+    elif w["kind"] == "greedy":
+        B, g = w["tokens"].shape
+        need = sv.sv_workspace_bytes_greedy(B, g, w["target"].shape[2])
+        outs = (torch.empty((B, g + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+
+        def step(s):
+            sv.spec_verify_greedy(s["target"], s["tokens"], ws=ws, out=outs)
+        kernel = "greedy_kernel"
+    else:
+        B, N = w["tokens"].shape
+        need = sv.sv_workspace_bytes_tree(B, N, w["target"].shape[2])
+        outs = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+
+        def step(s):
+            sv.spec_verify_tree_greedy(s["target"], s["tokens"], s["parents"], ws=ws, out=outs)
+        kernel = "greedy_kernel"
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    del bnd
+
+    for i in range(args.warmup):
+        step(sets[i % nrot])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # keep the GPU busy while the host queues the timed steps, so that the
+    # steps run back to back and the events time the GPU, not Python
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(args.queue_ahead_cycles))
+    t_all0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(sets[i % nrot])
+        ev[i][1].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    mean_launch_ms = float(np.mean(per_launch_ms))
+    ms_per_step = total_ms / K
+    rows = rows_per_step(w)
+    value = rows * K / (total_ms / 1e3)
+    achieved = nbytes / (mean_launch_ms / 1e3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            ent = tj.get(args.workload)
+            if ent and ent.get("kernel_sources_sha") == _sources_sha():
+                traffic = ent.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seqs)
+
+    dtype = "f32"
+    cfg = dict(workload=args.workload, desc=WORKLOADS[args.workload]["desc"],
+               logits_dtype=str(w["target"].dtype).replace("uint16", "bf16"),
+               rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
+               kernel=kernel, step_ms_median=float(np.median(per_launch_ms)),
+               step_ms_p10=float(np.percentile(per_launch_ms, 10)),
+               step_ms_p90=float(np.percentile(per_launch_ms, 90)),
+               seqs_per_s=float(w["target"].shape[0] * K / (total_ms / 1e3)))
+    line = dict(metric=METRIC, value=value, unit="rows/s", n_gpus=1, steps=K, warmup=args.warmup,
+                ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype=dtype, data="synthetic", config=cfg,
+                roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
+                              frac=achieved / PEAK_GBS, traffic=traffic),
+                cpu_baseline=cpu)
+    print(json.dumps(line), flush=True)
+
+
+def _sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "draft_token_verification_07_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

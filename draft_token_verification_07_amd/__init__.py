@@ -1,6 +1,14 @@
 """MI355X-native batched draft-token verification (speculative sampling).
 
 The compute path is the C-ABI library libspecverify.so (hand-written HIP for
-gfx950).  This package is its thin Python binding; see `binding` for the
-calls.  `synth` holds the seeded input generators.
+gfx950, declared in include/spec_verify.h).  This package is its thin Python
+binding (`binding`, re-exported here) plus the seeded input generators
+(`synth`).  Importing the package does not load the library; the first call
+does, and raises if it has not been built.
 """
+from .binding import (  # noqa: F401
+    SV_BF16, SV_F32, SV_MAX_GAMMA, SV_MAX_TREE_NODES, SV_MAX_VOCAB,
+    SV_SEQ_BAD_PARENT, SV_SEQ_NO_MASS, SV_SEQ_TOKEN_RANGE, SpecVerifyError, lib,
+    spec_verify_greedy, spec_verify_sample, spec_verify_tree_greedy,
+    sv_workspace_bytes_greedy, sv_workspace_bytes_sample, sv_workspace_bytes_tree,
+)

@@ -1,0 +1,248 @@
+"""Thin ctypes binding of libspecverify (the C ABI declared in include/spec_verify.h).
+
+Argument marshalling only: every step of verification runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  The
+library must be built (python -m draft_token_verification_07_amd._build);
+calling any entry point without it raises.
+
+    tokens, accept_len, p_tok, q_tok, status = spec_verify_sample(
+        target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+        temperature, top_p, d2t=None)
+    tokens, accept_len, status = spec_verify_greedy(target_logits, draft_tokens)
+    path, tokens, accept_len, status = spec_verify_tree_greedy(target_logits, node_tokens, parents)
+
+Tensors must live on the same GPU and be contiguous: logits float32 or
+bfloat16, token ids / d2t / parents int32, uniforms float32.  Outputs are
+new device tensors, written asynchronously on the current stream.  A
+workspace (zeroed once at allocation, reused afterwards) is kept per
+(device, stream) unless one is passed in.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+SV_SEQ_TOKEN_RANGE, SV_SEQ_NO_MASS, SV_SEQ_BAD_PARENT = 1, 4, 8
+SV_MAX_GAMMA, SV_MAX_TREE_NODES, SV_MAX_VOCAB = 255, 4096, 1 << 24
+
+_STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED_DTYPE",
+           3: "SV_ERR_WORKSPACE_TOO_SMALL", 4: "SV_ERR_HIP", 5: "SV_ERR_TOO_LARGE"}
+
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        msg = lib().spec_verify_strerror(code).decode() if _lib is not None else ""
+        super().__init__("%s failed: %s (%s)" % (fn, _STATUS.get(code, code), msg))
+        self.code = code
+
+
+def lib() -> C.CDLL:
+    """Load libspecverify.so (built in-tree).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        "libspecverify.so is not built (%s); run "
+                        "`python -m draft_token_verification_07_amd._build`" % LIB_PATH)
+                L = C.CDLL(LIB_PATH)
+                P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+                L.spec_verify_strerror.restype = C.c_char_p
+                L.spec_verify_strerror.argtypes = [C.c_int]
+                L.sv_workspace_bytes_sample.restype = sz
+                L.sv_workspace_bytes_sample.argtypes = [i32, i32, i32, i32, C.c_float]
+                L.sv_workspace_bytes_greedy.restype = sz
+                L.sv_workspace_bytes_greedy.argtypes = [i32, i32, i32]
+                L.sv_workspace_bytes_tree.restype = sz
+                L.sv_workspace_bytes_tree.argtypes = [i32, i32, i32]
+                L.spec_verify_sample.restype = C.c_int
+                L.spec_verify_sample.argtypes = [P, C.c_int, P, C.c_int, P, P, P, P, i32, i32, i32, i32,
+                                                 C.c_float, C.c_float, P, P, P, P, P, P, sz, P]
+                L.spec_verify_greedy.restype = C.c_int
+                L.spec_verify_greedy.argtypes = [P, C.c_int, P, i32, i32, i32, P, P, P, P, sz, P]
+                L.spec_verify_tree_greedy.restype = C.c_int
+                L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
+                _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError("logits must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _check(t: torch.Tensor, name: str, dev: torch.device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    """The cached workspace of the current (device, stream), grown to nbytes
+    and zeroed when (re)allocated.  Calls on one stream are ordered, so they
+    can share it; the kernels return it to zero."""
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def _raise(fn, code):
+    if code != 0:
+        raise SpecVerifyError(fn, code)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def sv_workspace_bytes_sample(B, gamma, Vt, Vd, top_p) -> int:
+    return int(lib().sv_workspace_bytes_sample(B, gamma, Vt, Vd, float(top_p)))
+
+
+def sv_workspace_bytes_greedy(B, gamma, V) -> int:
+    return int(lib().sv_workspace_bytes_greedy(B, gamma, V))
+
+
+def sv_workspace_bytes_tree(B, N, V) -> int:
+    return int(lib().sv_workspace_bytes_tree(B, N, V))
+
+
+def spec_verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                       temperature: float, top_p: float, d2t=None, *, want_probs: bool = True,
+                       ws: torch.Tensor | None = None, out=None):
+    """Sampling verification.  Returns (tokens [B, g+1], accept_len [B],
+    p_tok [B, g] | None, q_tok [B, g] | None, status [B]) as device tensors."""
+    L = lib()
+    dev = target_logits.device
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, Vt]")
+    B, g1, Vt = target_logits.shape
+    g = g1 - 1
+    _check(target_logits, "target_logits", dev)
+    tdt = _dtype_code(target_logits)
+    if g > 0:
+        _check(draft_logits, "draft_logits", dev)
+        if draft_logits.dim() != 3 or tuple(draft_logits.shape[:2]) != (B, g):
+            raise ValueError("draft_logits must be [B, gamma, Vd]")
+        Vd = draft_logits.shape[2]
+        ddt = _dtype_code(draft_logits)
+        _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, g))
+        _check(u_accept, "u_accept", dev, torch.float32, (B, g))
+    else:
+        Vd = Vt if d2t is None else d2t.shape[0]
+        ddt = tdt if draft_logits is None else _dtype_code(draft_logits)
+    _check(u_sample, "u_sample", dev, torch.float32, (B,))
+    if d2t is not None:
+        _check(d2t, "d2t", dev, torch.int32, (Vd,))
+    if out is None:
+        out_tokens = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        out_p = torch.empty((B, g), dtype=torch.float32, device=dev) if want_probs else None
+        out_q = torch.empty((B, g), dtype=torch.float32, device=dev) if want_probs else None
+        out_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        out_tokens, out_len, out_p, out_q, out_status = out
+    need = sv_workspace_bytes_sample(B, g, Vt, Vd, top_p)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_verify_sample(
+        _ptr(target_logits), tdt, _ptr(draft_logits if g > 0 else None), ddt,
+        _ptr(draft_tokens if g > 0 else None), _ptr(d2t), _ptr(u_accept if g > 0 else None), _ptr(u_sample),
+        B, g, Vt, Vd, float(temperature), float(top_p),
+        _ptr(out_tokens), _ptr(out_len), _ptr(out_p), _ptr(out_q), _ptr(out_status),
+        _ptr(ws), ws.numel(), _stream(dev))
+    _raise("spec_verify_sample", rc)
+    return out_tokens, out_len, out_p, out_q, out_status
+
+
+def spec_verify_greedy(target_logits, draft_tokens, *, ws: torch.Tensor | None = None, out=None):
+    """Greedy verification.  Returns (tokens [B, g+1], accept_len [B], status [B])."""
+    L = lib()
+    dev = target_logits.device
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, V]")
+    B, g1, V = target_logits.shape
+    g = g1 - 1
+    _check(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    if g > 0:
+        _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, g))
+    if out is None:
+        out_tokens = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        out_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        out_tokens, out_len, out_status = out
+    need = sv_workspace_bytes_greedy(B, g, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_verify_greedy(_ptr(target_logits), dt, _ptr(draft_tokens if g > 0 else None), B, g, V,
+                              _ptr(out_tokens), _ptr(out_len), _ptr(out_status), _ptr(ws), ws.numel(),
+                              _stream(dev))
+    _raise("spec_verify_greedy", rc)
+    return out_tokens, out_len, out_status
+
+
+def spec_verify_tree_greedy(target_logits, node_tokens, parents, *, ws: torch.Tensor | None = None, out=None):
+    """Greedy tree verification.  Returns (path [B, N], tokens [B, N], accept_len [B], status [B])."""
+    L = lib()
+    dev = target_logits.device
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, N, V]")
+    B, N, V = target_logits.shape
+    _check(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    _check(node_tokens, "node_tokens", dev, torch.int32, (B, N))
+    _check(parents, "parents", dev, torch.int32, (B, N))
+    if out is None:
+        out_path = torch.empty((B, N), dtype=torch.int32, device=dev)
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+        out_len = torch.empty((B,), dtype=torch.int32, device=dev)
+        out_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        out_path, out_tokens, out_len, out_status = out
+    need = sv_workspace_bytes_tree(B, N, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_verify_tree_greedy(_ptr(target_logits), dt, _ptr(node_tokens), _ptr(parents), B, N, V,
+                                   _ptr(out_path), _ptr(out_tokens), _ptr(out_len), _ptr(out_status),
+                                   _ptr(ws), ws.numel(), _stream(dev))
+    _raise("spec_verify_tree_greedy", rc)
+    return out_path, out_tokens, out_len, out_status

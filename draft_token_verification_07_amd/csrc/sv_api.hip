@@ -1,0 +1,187 @@
+// sv_api.hip -- the C ABI of libspecverify: argument checks, workspace
+// sizing and launch dispatch.  No allocation, no synchronization: every
+// launch goes to the caller's stream, and host-detectable argument errors
+// return before anything is launched.
+#include <math.h>
+#include <stdint.h>
+
+#include "sv_common.h"
+#include "sv_internal.h"
+
+using namespace sv;
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16; }
+size_t esize(int dt) { return dt == SV_BF16 ? 2 : 4; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The whole grid must fit one launch dimension.
+bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
+
+size_t greedy_ws(int32_t B, int32_t R, int32_t V) {
+    const int32_t C = greedy_chunks(V, SV_BF16);
+    size_t off = align256(sizeof(uint32_t) * (size_t)B);            // counters
+    off += align256(sizeof(int32_t) * 2 * (size_t)B * R * C);       // (value, index) partials
+    return off < 256 ? 256 : off;                                   // never 0: 0 means invalid sizes
+}
+
+sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, const int32_t *parents,
+                     int32_t B, int32_t R, int32_t V, bool tree, int32_t *out_tokens, int32_t *out_len,
+                     int32_t *out_status, int32_t *out_path, void *ws, size_t ws_bytes, hipStream_t st) {
+    GreedyArgs a;
+    a.logits = logits;
+    a.tokens = tokens;
+    a.parents = parents;
+    a.B = B;
+    a.rows_per_seq = R;
+    a.V = V;
+    a.chunks = greedy_chunks(V, dt);
+    a.tree = tree ? 1 : 0;
+    a.out_tokens = out_tokens;
+    a.out_len = out_len;
+    a.out_status = out_status;
+    a.out_path = out_path;
+    char *base = static_cast<char *>(ws);
+    a.counters = reinterpret_cast<uint32_t *>(base);
+    a.part = reinterpret_cast<ArgMax *>(base + align256(sizeof(uint32_t) * (size_t)B));
+    if (!grid_fits((int64_t)B * R * a.chunks)) return SV_ERR_TOO_LARGE;
+    (void)ws_bytes;
+    return launch_greedy(a, dt, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_verify_strerror(sv_status s) {
+    switch (s) {
+        case SV_OK: return "ok";
+        case SV_ERR_INVALID_ARG: return "invalid argument";
+        case SV_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+        case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SV_ERR_HIP: return "HIP launch error";
+        case SV_ERR_TOO_LARGE: return "size beyond library limits";
+    }
+    return "unknown status";
+}
+
+size_t sv_workspace_bytes_greedy(int32_t B, int32_t gamma, int32_t V) {
+    if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
+    return greedy_ws(B, gamma + 1, V);
+}
+
+size_t sv_workspace_bytes_tree(int32_t B, int32_t N, int32_t V) {
+    if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return 0;
+    return greedy_ws(B, N, V);
+}
+
+size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, float top_p) {
+    if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || Vt < 1 || Vd < 1 || Vt > SV_MAX_VOCAB ||
+        Vd > SV_MAX_VOCAB || !(top_p > 0.0f))
+        return 0;
+    WorkspaceLayout L;
+    int32_t ct, cd, nt;
+    sample_layout(B, gamma, Vt, Vd, SV_BF16, SV_BF16, top_p < 1.0f, &L, &ct, &cd, &nt);
+    return L.total;
+}
+
+sv_status spec_verify_greedy(const void *target_logits, sv_dtype dtype, const int32_t *draft_tokens,
+                             int32_t B, int32_t gamma, int32_t V, int32_t *out_tokens,
+                             int32_t *out_accept_len, int32_t *out_status, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+    if (B < 0 || gamma < 0 || V < 1) return SV_ERR_INVALID_ARG;
+    if (gamma > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !out_tokens || !out_accept_len || !workspace) return SV_ERR_INVALID_ARG;
+    if (gamma > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
+    if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
+    if (workspace_bytes < sv_workspace_bytes_greedy(B, gamma, V)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    return run_greedy(target_logits, dtype, draft_tokens, nullptr, B, gamma + 1, V, false, out_tokens,
+                      out_accept_len, out_status, nullptr, workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_tree_greedy(const void *target_logits, sv_dtype dtype, const int32_t *node_tokens,
+                                  const int32_t *parents, int32_t B, int32_t N, int32_t V,
+                                  int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
+                                  int32_t *out_status, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+    if (B < 0 || N < 1 || V < 1) return SV_ERR_INVALID_ARG;
+    if (N > SV_MAX_TREE_NODES || V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len ||
+        !workspace)
+        return SV_ERR_INVALID_ARG;
+    if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
+    if (workspace_bytes < sv_workspace_bytes_tree(B, N, V)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    return run_greedy(target_logits, dtype, node_tokens, parents, B, N, V, true, out_tokens, out_accept_len,
+                      out_status, out_path_nodes, workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
+                             sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
+                             const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,
+                             int32_t Vt, int32_t Vd, float temperature, float top_p, int32_t *out_tokens,
+                             int32_t *out_accept_len, float *out_p_tok, float *out_q_tok, int32_t *out_status,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(target_dtype) || !dtype_ok(draft_dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+    if (B < 0 || gamma < 0 || Vt < 1 || Vd < 1) return SV_ERR_INVALID_ARG;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
+    if (!(top_p > 0.0f)) return SV_ERR_INVALID_ARG;          // also rejects NaN
+    if (!d2t && Vd != Vt) return SV_ERR_INVALID_ARG;
+    if (d2t && Vd > Vt) return SV_ERR_INVALID_ARG;            // an injective map needs Vd <= Vt
+    if (gamma > SV_MAX_GAMMA || Vt > SV_MAX_VOCAB || Vd > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !u_sample || !out_tokens || !out_accept_len || !workspace) return SV_ERR_INVALID_ARG;
+    if (gamma > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
+    if (!aligned(target_logits, esize(target_dtype))) return SV_ERR_INVALID_ARG;
+    if (gamma > 0 && !aligned(draft_logits, esize(draft_dtype))) return SV_ERR_INVALID_ARG;
+
+    const bool topp = top_p < 1.0f;
+    WorkspaceLayout L;
+    int32_t Ct, Cd, nt;
+    sample_layout(B, gamma, Vt, Vd, target_dtype, draft_dtype, topp, &L, &Ct, &Cd, &nt);
+    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE_TOO_SMALL;
+    const int64_t NR = 2 * (int64_t)gamma + 1;
+    if (!grid_fits((int64_t)B * (topp ? NR : ((int64_t)(gamma + 1) * Ct + (int64_t)gamma * Cd))) ||
+        !grid_fits((int64_t)B * nt))
+        return SV_ERR_TOO_LARGE;
+
+    SampleArgs a;
+    a.tl = target_logits;
+    a.dl = draft_logits;
+    a.tokens = draft_tokens;
+    a.d2t = d2t;
+    a.u_acc = u_accept;
+    a.u_s = u_sample;
+    a.B = B;
+    a.gamma = gamma;
+    a.Vt = Vt;
+    a.Vd = Vd;
+    a.T = temperature;
+    a.c = 1.4426950408889634f / temperature;     // log2(e) / T: 2^((z - m) c) = e^((z - m) / T)
+    a.top_p = top_p;
+    a.topp = topp ? 1 : 0;
+    a.Ct = Ct;
+    a.Cd = Cd;
+    a.ntiles = nt;
+    a.out_tokens = out_tokens;
+    a.out_len = out_accept_len;
+    a.out_status = out_status;
+    a.out_p = out_p_tok;
+    a.out_q = out_q_tok;
+    char *base = static_cast<char *>(workspace);
+    a.cnt_stats = reinterpret_cast<uint32_t *>(base + L.cnt_stats);
+    a.cnt_draw = reinterpret_cast<uint32_t *>(base + L.cnt_draw);
+    a.seq = reinterpret_cast<SeqState *>(base + L.seq);
+    a.rows = reinterpret_cast<RowDesc *>(base + L.rows);
+    a.part = reinterpret_cast<MaxSum *>(base + L.part);
+    a.kept = reinterpret_cast<KeptEnt *>(base + L.kept);
+    a.tile_mass = reinterpret_cast<float *>(base + L.tile_mass);
+    return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+// sv_common.h -- device helpers shared by the verification kernels (gfx950).
+//
+// Row streaming: a logits row is read once from HBM with 16-byte vector loads
+// (8 bfloat16 or 4 float32 per lane), fully coalesced across the wave.  A row
+// may start at any element-aligned address: the elements before the first
+// 16-byte boundary (the head) and after the last full vector (the tail) are
+// read one by one.  Each lane visits its elements in increasing index order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// A native 16-byte vector (the HIP uint4 struct is not accepted by the
+// nontemporal-load builtin).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element decoding.  bfloat16 widens to float32 exactly (it is the high half).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int DT> struct Elem;
+template <> struct Elem<SV_F32> {
+    static constexpr int kBytes = 4;
+    static constexpr int kPerVec = 4;
+    __device__ __forceinline__ static float load(const void *base, int64_t i) {
+        return reinterpret_cast<const float *>(base)[i];
+    }
+    __device__ __forceinline__ static void unpack(const u32x4 &v, float (&o)[kPerVec]) {
+        o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+        o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+    }
+};
+template <> struct Elem<SV_BF16> {
+    static constexpr int kBytes = 2;
+    static constexpr int kPerVec = 8;
+    __device__ __forceinline__ static float load(const void *base, int64_t i) {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(base)[i] << 16);
+    }
+    __device__ __forceinline__ static void unpack(const u32x4 &v, float (&o)[kPerVec]) {
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+};
+
+// Order-preserving unsigned key of a float32 (larger float -> larger key;
+// -0 and +0 get different keys, so callers compare VALUES where they must be equal).
+__device__ __forceinline__ uint32_t fkey(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ---------------------------------------------------------------------------
+// Row geometry: head / 16-byte vector body / tail split of one row.
+// ---------------------------------------------------------------------------
+struct RowSplit {
+    int32_t head;     // scalar elements before the first 16-byte boundary
+    int32_t nvec;     // full 16-byte vectors
+    int32_t tail;     // scalar elements after the body
+};
+
+template <int DT>
+__device__ __forceinline__ RowSplit row_split(const void *row, int32_t len) {
+    using E = Elem<DT>;
+    uintptr_t a = reinterpret_cast<uintptr_t>(row);
+    int32_t head = (int32_t)(((16u - (uint32_t)(a & 15u)) & 15u) / E::kBytes);
+    if (head > len) head = len;
+    int32_t nvec = (len - head) / E::kPerVec;
+    RowSplit s;
+    s.head = head;
+    s.nvec = nvec;
+    s.tail = len - head - nvec * E::kPerVec;
+    return s;
+}
+
+// Visit the elements [lo_vec, hi_vec) of the vector body, plus the head when
+// `with_head` and the tail when `with_tail`, calling f(value, index) with
+// indices increasing per lane.  U vectors are loaded per lane before any is
+// used, so U * 16 bytes per lane are in flight.
+template <int DT, int U, int NT, typename F>
+__device__ __forceinline__ void stream_row(const void *row, const RowSplit &s, int32_t lo_vec,
+                                           int32_t hi_vec, bool with_head, bool with_tail, F &&f) {
+    using E = Elem<DT>;
+    const int tid = threadIdx.x;
+    if (with_head && tid < s.head) f(E::load(row, tid), tid);
+    const u32x4 *body = reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const char *>(row) + (size_t)s.head * E::kBytes);
+    int32_t v = lo_vec + tid;
+    // full iterations: every lane has U vectors
+    for (; v + (U - 1) * NT < hi_vec; v += U * NT) {
+        u32x4 buf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load(&body[v + u * NT]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[E::kPerVec];
+            E::unpack(buf[u], x);
+            const int32_t i0 = s.head + (v + u * NT) * E::kPerVec;
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) f(x[k], i0 + k);
+        }
+    }
+    // ragged last iteration
+    for (; v < hi_vec; v += NT) {
+        float x[E::kPerVec];
+        E::unpack(__builtin_nontemporal_load(&body[v]), x);
+        const int32_t i0 = s.head + v * E::kPerVec;
+#pragma unroll
+        for (int k = 0; k < E::kPerVec; ++k) f(x[k], i0 + k);
+    }
+    if (with_tail && tid < s.tail) {
+        const int32_t i = s.head + s.nvec * E::kPerVec + tid;
+        f(E::load(row, i), i);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Wave / workgroup reductions (wave64).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        T w = __shfl_xor(v, o, kWave);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// Argmax pair: larger value wins; equal values go to the lower index.
+struct ArgMax {
+    float v;
+    int32_t i;
+};
+__device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
+    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        ArgMax b;
+        b.v = __shfl_xor(a.v, o, kWave);
+        b.i = __shfl_xor(a.i, o, kWave);
+        a = argmax_merge(a, b);
+    }
+    return a;
+}
+
+// Online softmax partial: s = sum over the elements of 2^((z - m) * c).
+struct MaxSum {
+    float m;
+    float s;
+};
+__device__ __forceinline__ MaxSum maxsum_merge(MaxSum a, MaxSum b, float c) {
+    if (b.m > a.m) { MaxSum t = a; a = b; b = t; }
+    if (b.m == -INFINITY) return a;            // also covers a.m == b.m == -inf
+    a.s = a.s + b.s * exp2f((b.m - a.m) * c);
+    return a;
+}
+__device__ __forceinline__ MaxSum wave_maxsum(MaxSum a, float c) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        MaxSum b;
+        b.m = __shfl_xor(a.m, o, kWave);
+        b.s = __shfl_xor(a.s, o, kWave);
+        a = maxsum_merge(a, b, c);
+    }
+    return a;
+}
+
+// Inclusive prefix sum of doubles across a wave (lane order).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double w = __shfl_up(v, o, kWave);
+        if (lane >= o) v += w;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Last-arriving workgroup.  Every workgroup of a group publishes its partial
+// results, fences them to device scope, then bumps the group's counter; the
+// workgroup that brings the counter to `total` continues with the group's
+// combine step and returns the counter to zero for the next call.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, int *flag_smem) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t prev = atomicAdd(counter, 1u);
+        int last = (prev == total - 1u);
+        if (last) atomicExch(counter, 0u);
+        *flag_smem = last;
+    }
+    __syncthreads();
+    const bool last = *flag_smem != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+}  // namespace sv

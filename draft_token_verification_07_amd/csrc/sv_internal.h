@@ -1,0 +1,146 @@
+// sv_internal.h -- kernel argument blocks, workspace layout and launch
+// tuning shared by the C-ABI front end and the kernels.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+
+namespace sv {
+
+struct ArgMax;
+struct MaxSum;
+
+// ---------------------------------------------------------------------------
+// Tuning (chosen by measurement on MI355X; see the design notes).
+// ---------------------------------------------------------------------------
+#ifndef SV_GREEDY_THREADS
+#define SV_GREEDY_THREADS 256
+#endif
+#ifndef SV_GREEDY_UNROLL
+#define SV_GREEDY_UNROLL 4
+#endif
+#ifndef SV_GREEDY_ITERS
+#define SV_GREEDY_ITERS 4
+#endif
+#ifndef SV_STATS_THREADS
+#define SV_STATS_THREADS 256
+#endif
+#ifndef SV_STATS_UNROLL
+#define SV_STATS_UNROLL 4
+#endif
+#ifndef SV_STATS_ITERS
+#define SV_STATS_ITERS 4
+#endif
+#ifndef SV_TOPP_THREADS
+#define SV_TOPP_THREADS 512
+#endif
+#ifndef SV_TOPP_UNROLL
+#define SV_TOPP_UNROLL 4
+#endif
+
+constexpr int kGreedyThreads = SV_GREEDY_THREADS;
+constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
+constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
+constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
+constexpr int kStatsUnroll = SV_STATS_UNROLL;
+constexpr int kStatsItersPerWg = SV_STATS_ITERS;
+constexpr int kToppThreads = SV_TOPP_THREADS;       // one workgroup per row with top-p
+constexpr int kToppUnroll = SV_TOPP_UNROLL;
+constexpr int kSampThreads = 256;                   // residual / bonus draw
+constexpr int kMaxChunks = 4096;
+
+// Top-p candidate band: during streaming a token is kept in LDS when its
+// logit is within kToppBandNats * T of the running row maximum (so
+// y = z / T is within kToppBandNats of max y).  At the end the band is
+// verified to hold more than top_p of the row's mass; otherwise the row
+// takes the exact radix-select path over the whole row.
+constexpr float kToppBandNats = 9.0f;
+constexpr int kCandCap = 4096;      // LDS candidate slots per row (power of two)
+constexpr int kKeptCap = 4096;      // kept-list entries stored per row
+constexpr int kTile = 4096;         // target ids per residual/bonus tile
+
+// ---------------------------------------------------------------------------
+// Greedy / tree
+// ---------------------------------------------------------------------------
+struct GreedyArgs {
+    const void *logits;
+    const int32_t *tokens;     // chain: [B, gamma]; tree: [B, N]
+    const int32_t *parents;    // tree only: [B, N]
+    int32_t B, rows_per_seq, V, chunks;
+    int32_t tree;
+    int32_t *out_tokens, *out_len, *out_status, *out_path;
+    ArgMax *part;              // [B * rows_per_seq * chunks]
+    uint32_t *counters;        // [B]
+};
+
+int32_t greedy_chunks(int32_t V, int dtype);
+hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Sampling
+// ---------------------------------------------------------------------------
+
+// Per-row distribution descriptor.  Token id j of the row (own vocabulary)
+// with logit z has weight w = 2^((z - m) * c), c = log2(e) / T.  It is kept
+// iff key(z) > key || (key(z) == key && j <= tie_cut), where key() is the
+// order-preserving key of z with -0 folded onto +0; without top-p key = 0 and
+// tie_cut = INT32_MAX keep every id.  p(j) = w / Zk for kept ids, else 0.
+struct RowDesc {
+    float m;          // row maximum of the raw logits
+    float Z;          // sum of w over the whole row
+    float Zk;         // sum of w over the kept ids
+    uint32_t key;
+    int32_t tie_cut;
+    int32_t nkept;    // kept ids; the list is stored iff nkept <= kKeptCap
+    int32_t flags;    // RD_* bits
+    int32_t pad;
+};
+enum { RD_NO_MASS = 1, RD_HAS_LIST = 2, RD_FALLBACK = 4 };
+
+struct KeptEnt {      // one kept id of a row and its weight w
+    int32_t id;
+    float w;
+};
+
+struct SeqState {     // written by the statistics epilogue for the draw kernel
+    int32_t n;        // accepted drafts
+    int32_t status;   // SV_SEQ_* bits
+    int32_t pad0, pad1;
+};
+
+struct SampleArgs {
+    const void *tl;            // target logits [B, gamma+1, Vt]
+    const void *dl;            // draft logits  [B, gamma, Vd]
+    const int32_t *tokens;     // [B, gamma]
+    const int32_t *d2t;        // [Vd] or null
+    const float *u_acc;        // [B, gamma]
+    const float *u_s;          // [B]
+    int32_t B, gamma, Vt, Vd;
+    float T, c, top_p;         // c = log2(e) / T
+    int32_t topp;              // top-p filter on
+    int32_t Ct, Cd;            // chunks per target / draft row (1 with top-p)
+    int32_t ntiles;            // draw tiles per sequence (plain mode)
+    int32_t *out_tokens, *out_len, *out_status;
+    float *out_p, *out_q;
+    // workspace
+    uint32_t *cnt_stats;       // [B]
+    uint32_t *cnt_draw;        // [B]
+    SeqState *seq;             // [B]
+    RowDesc *rows;             // [B, 2*gamma+1]: target rows then draft rows
+    MaxSum *part;              // [B, (gamma+1)*Ct + gamma*Cd]
+    KeptEnt *kept;             // [B, 2*gamma+1, kKeptCap] (top-p only)
+    float *tile_mass;          // [B, ntiles]
+};
+
+struct WorkspaceLayout {
+    size_t cnt_stats, cnt_draw, seq, rows, part, kept, tile_mass, total;
+};
+bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int dt_t, int dt_d, bool topp,
+                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *ntiles);
+int32_t stats_chunks(int32_t V, int dtype);
+hipError_t launch_sample(const SampleArgs &a, int dt_t, int dt_d, hipStream_t st);
+
+}  // namespace sv

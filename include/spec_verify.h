@@ -1,0 +1,190 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify, batched draft-token verification
+ * (speculative sampling) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are cited by page title and section):
+ *   "Ling-3.0-flash-dspark" draft-model tutorial (mlqm.cn/news/1205650):
+ *     sec. 3.1 -- the draft proposes gamma tokens; the target scores gamma+1
+ *       positions in one pass; draft token i is accepted with probability
+ *       min(1, p_i(x_i) / q_i(x_i)); the first rejection is replaced by a draw
+ *       from norm(max(0, p - q)) and the later drafts are dropped; when every
+ *       draft is accepted an extra token is drawn from the last target row.
+ *     sec. 4.2 -- both distributions are softmax(logits / temperature) after
+ *       the same top-p filter (_apply_top_p), p from the target rows, q from
+ *       the draft rows.
+ *     sec. 6.2 -- batching: every sequence keeps its own acceptance position.
+ *     sec. 6.4 -- draft length 0 is a boundary case (bonus draw only).
+ *   SSD inference-engine guide (lpnh.cn/news/2716086):
+ *     sec. 6 -- an EAGLE3 draft head covers a reduced vocabulary that d2t maps
+ *       into the target vocabulary; ids off the map have draft probability 0.
+ *     sec. 7 -- temperature-0 runs: greedy verification.
+ *   "基于1层Llama草稿模型实现2.16推测解码加速" (the 2.16x EAGLE blog):
+ *     sec. 5 -- a draft tree (32 nodes, depth 5, top-k 8) verified by one target
+ *       pass; the speed-up table's Match = True asks for output identical to
+ *       the target's own greedy decoding.
+ *
+ * Readings fixed where the pages leave a step open:
+ *   - Each sequence supplies its uniforms: u_accept[b, i] for the accept test
+ *     of draft i and one u_sample[b] for whichever draw (replacement or bonus)
+ *     happens.  The accept test is u * q < p (the q = 0 limit accepts iff p > 0).
+ *   - Draws are inverse-CDF in ascending token id: the first id whose
+ *     inclusive cumulative weight exceeds u * (total weight).
+ *   - Top-p keeps sorted position s >= 1 iff the cumulative softmax of
+ *     positions < s is <= top_p; equal logits are ordered by lower id first.
+ *     top_p >= 1 switches the filter off.
+ *   - Argmax ties go to the lowest id; -0 and +0 are equal.
+ *   - Tree: the deepest accepted node wins, ties to the lowest node index.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, never synchronizes, and enqueues its kernels on
+ *     `stream` only (0 = the null stream).  Outputs are written by the kernels;
+ *     they are valid once the stream reaches that point.
+ *   - Layouts are row-major and contiguous.  Logits rows may have any length
+ *     and alignment (only element alignment is required).
+ *   - Host-detectable argument errors return an sv_status != SV_OK with NO
+ *     launch.  A failed launch returns SV_ERR_HIP.  No C++ exception crosses
+ *     the ABI.
+ *   - Device-detected per-sequence conditions are reported in out_status[b]
+ *     (when out_status is not NULL) as SV_SEQ_* bits; the call still completes.
+ *   - The workspace is caller memory of at least sv_workspace_bytes_*() bytes
+ *     that must be ZEROED ONCE when allocated.  Every call returns its
+ *     counters to zero, so the same workspace serves later calls on the same
+ *     stream.  Calls that may run concurrently need separate workspaces.
+ *     After a call that failed on the device, zero the workspace again.
+ *   - Inputs containing NaN are outside the contract; -inf logits (masked
+ *     tokens) are allowed.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1,         /* a null pointer, a size out of range, a bad scalar  */
+    SV_ERR_UNSUPPORTED_DTYPE = 2,   /* a dtype code other than SV_F32 / SV_BF16            */
+    SV_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below sv_workspace_bytes_*()       */
+    SV_ERR_HIP = 4,                 /* the HIP runtime reported an error at launch        */
+    SV_ERR_TOO_LARGE = 5            /* a size beyond the library's documented limits      */
+} sv_status;
+
+typedef enum {
+    SV_F32 = 0,    /* IEEE float32 */
+    SV_BF16 = 1    /* bfloat16 (the high 16 bits of a float32) */
+} sv_dtype;
+
+/* out_status bits (per sequence). */
+#define SV_SEQ_TOKEN_RANGE 1  /* a draft/node token id outside [0, V): treated as p = q = 0 (rejected / unmatched) */
+#define SV_SEQ_NO_MASS     4  /* a logits row whose maximum is not finite; draws from it return -1             */
+#define SV_SEQ_BAD_PARENT  8  /* tree: parents[b][k] outside [0, k) for k >= 1; that node is never accepted     */
+
+/* Limits.  Sizes beyond them return SV_ERR_TOO_LARGE. */
+#define SV_MAX_GAMMA      255       /* draft tokens per sequence                     */
+#define SV_MAX_TREE_NODES 4096      /* nodes per tree                                */
+#define SV_MAX_VOCAB      (1 << 24) /* logits row length (target and draft)          */
+
+/*
+ * Workspace sizes in bytes for a call with these sizes (0 only for invalid sizes).
+ * The result depends only on the arguments, so a workspace sized for the
+ * largest call serves every smaller one.
+ */
+size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, float top_p);
+size_t sv_workspace_bytes_greedy(int32_t B, int32_t gamma, int32_t V);
+size_t sv_workspace_bytes_tree(int32_t B, int32_t N, int32_t V);
+
+/*
+ * Sampling verification (Ling tutorial sec. 3.1 and sec. 4.2; SSD guide sec. 6
+ * for d2t).
+ *
+ *   target_logits  [B, gamma+1, Vt] of target_dtype.  Row i (< gamma) is the
+ *                  target's distribution for draft token i; row gamma is the
+ *                  bonus position.
+ *   draft_logits   [B, gamma, Vd] of draft_dtype.  May be NULL when gamma == 0.
+ *   draft_tokens   [B, gamma] int32, TARGET-vocabulary ids.  May be NULL when gamma == 0.
+ *   d2t            [Vd] int32, strictly increasing ids in [0, Vt): draft id j
+ *                  is target id d2t[j].  NULL means Vd == Vt and the identity.
+ *                  (A map that is not strictly increasing or leaves [0, Vt) is
+ *                  outside the contract: results are undefined, memory safe.)
+ *   u_accept       [B, gamma] float32 in [0, 1).  May be NULL when gamma == 0.
+ *   u_sample       [B] float32 in [0, 1).
+ *   temperature    > 0 and finite (temperature 0 is spec_verify_greedy).
+ *   top_p          in (0, 1) filters p and q alike; >= 1 switches top-p off.
+ *   out_tokens     [B, gamma+1] int32: the accepted drafts, then the drawn
+ *                  token, then -1 padding.
+ *   out_accept_len [B] int32 in [0, gamma].
+ *   out_p_tok, out_q_tok  [B, gamma] float32 or NULL: p_i(x_i) and q_i(x_i)
+ *                  for every i < gamma (also past the first rejection).
+ *   out_status     [B] int32 or NULL: SV_SEQ_* bits.
+ *   workspace      >= sv_workspace_bytes_sample(B, gamma, Vt, Vd, top_p) bytes.
+ * Errors: SV_ERR_INVALID_ARG (null required pointer, B < 0, gamma < 0, V < 1,
+ * Vd != Vt without d2t, temperature <= 0 or not finite, top_p <= 0 or NaN),
+ * SV_ERR_UNSUPPORTED_DTYPE, SV_ERR_TOO_LARGE, SV_ERR_WORKSPACE_TOO_SMALL,
+ * SV_ERR_HIP.  B == 0 returns SV_OK without a launch.
+ */
+sv_status spec_verify_sample(
+    const void *target_logits, sv_dtype target_dtype,
+    const void *draft_logits, sv_dtype draft_dtype,
+    const int32_t *draft_tokens, const int32_t *d2t,
+    const float *u_accept, const float *u_sample,
+    int32_t B, int32_t gamma, int32_t Vt, int32_t Vd,
+    float temperature, float top_p,
+    int32_t *out_tokens, int32_t *out_accept_len,
+    float *out_p_tok, float *out_q_tok, int32_t *out_status,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy (temperature 0) verification (SSD guide sec. 7; EAGLE blog table).
+ *   target_logits  [B, gamma+1, V] of dtype; g_i = argmax of row i (lowest id on ties).
+ *   draft_tokens   [B, gamma] int32.  May be NULL when gamma == 0.
+ *   out_tokens     [B, gamma+1] int32: x_0..x_{n-1}, g_n, then -1 padding,
+ *                  where n is the first i with x_i != g_i (gamma if none).
+ *   out_accept_len [B] int32 = n.   out_status [B] int32 or NULL.
+ *   workspace      >= sv_workspace_bytes_greedy(B, gamma, V) bytes.
+ * Errors as for spec_verify_sample where they apply.
+ */
+sv_status spec_verify_greedy(
+    const void *target_logits, sv_dtype dtype,
+    const int32_t *draft_tokens, int32_t B, int32_t gamma, int32_t V,
+    int32_t *out_tokens, int32_t *out_accept_len, int32_t *out_status,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy tree verification (EAGLE blog sec. 5).
+ *   target_logits  [B, N, V] of dtype; row k is the target's distribution
+ *                  after node k (node 0 is the root, the last committed token).
+ *   node_tokens    [B, N] int32; entry 0 (the root) is ignored.
+ *   parents        [B, N] int32; parents[b][0] is ignored; 0 <= parents[b][k] < k.
+ *   Node k is accepted iff its parent is accepted (the root always is) and
+ *   node_tokens[b][k] equals the argmax of the parent's row.  The deepest
+ *   accepted node wins (ties to the lowest index).
+ *   out_path_nodes [B, N] int32: node indices of the root->winner path, root
+ *                  excluded, then -1 padding.
+ *   out_tokens     [B, N] int32: the path's tokens, then the argmax of the
+ *                  winner's row (the bonus), then -1 padding.
+ *   out_accept_len [B] int32: depth of the winner.   out_status [B] or NULL.
+ *   workspace      >= sv_workspace_bytes_tree(B, N, V) bytes.
+ * Errors as for spec_verify_sample where they apply; N must be >= 1.
+ */
+sv_status spec_verify_tree_greedy(
+    const void *target_logits, sv_dtype dtype,
+    const int32_t *node_tokens, const int32_t *parents,
+    int32_t B, int32_t N, int32_t V,
+    int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
+    int32_t *out_status, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char *spec_verify_strerror(sv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */
