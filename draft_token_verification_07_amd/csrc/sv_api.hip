@@ -15,16 +15,17 @@ namespace {
 bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16; }
 size_t esize(int dt) { return dt == SV_BF16 ? 2 : 4; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The whole grid must fit one launch dimension.
 bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
 
+// greedy / tree: counters [B] below K, (value, index) partials [B, R, C] above
+size_t greedy_counter_bytes(int32_t B) { return align256(sizeof(uint32_t) * (size_t)B); }
+size_t greedy_data_bytes(int32_t B, int32_t R, int32_t V) {
+    return align256(sizeof(int32_t) * 2 * (size_t)B * R * greedy_chunks(V, SV_BF16));
+}
 size_t greedy_ws(int32_t B, int32_t R, int32_t V) {
-    const int32_t C = greedy_chunks(V, SV_BF16);
-    size_t off = align256(sizeof(uint32_t) * (size_t)B);            // counters
-    off += align256(sizeof(int32_t) * 2 * (size_t)B * R * C);       // (value, index) partials
-    return off < 256 ? 256 : off;                                   // never 0: 0 means invalid sizes
+    return workspace_need(greedy_counter_bytes(B), greedy_data_bytes(B, R, V));
 }
 
 sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, const int32_t *parents,
@@ -43,11 +44,12 @@ sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, con
     a.out_len = out_len;
     a.out_status = out_status;
     a.out_path = out_path;
+    if (!workspace_fits(ws_bytes, greedy_counter_bytes(B), greedy_data_bytes(B, R, V)))
+        return SV_ERR_WORKSPACE_TOO_SMALL;
     char *base = static_cast<char *>(ws);
     a.counters = reinterpret_cast<uint32_t *>(base);
-    a.part = reinterpret_cast<ArgMax *>(base + align256(sizeof(uint32_t) * (size_t)B));
+    a.part = reinterpret_cast<ArgMax *>(base + counter_region(ws_bytes));
     if (!grid_fits((int64_t)B * R * a.chunks)) return SV_ERR_TOO_LARGE;
-    (void)ws_bytes;
     return launch_greedy(a, dt, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -84,7 +86,7 @@ size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t V
     WorkspaceLayout L;
     int32_t ct, cd, nt;
     sample_layout(B, gamma, Vt, Vd, SV_BF16, SV_BF16, top_p < 1.0f, &L, &ct, &cd, &nt);
-    return L.total;
+    return workspace_need(L.counter_bytes, L.data_bytes);
 }
 
 sv_status spec_verify_greedy(const void *target_logits, sv_dtype dtype, const int32_t *draft_tokens,
@@ -98,7 +100,6 @@ sv_status spec_verify_greedy(const void *target_logits, sv_dtype dtype, const in
     if (!target_logits || !out_tokens || !out_accept_len || !workspace) return SV_ERR_INVALID_ARG;
     if (gamma > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
     if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
-    if (workspace_bytes < sv_workspace_bytes_greedy(B, gamma, V)) return SV_ERR_WORKSPACE_TOO_SMALL;
     return run_greedy(target_logits, dtype, draft_tokens, nullptr, B, gamma + 1, V, false, out_tokens,
                       out_accept_len, out_status, nullptr, workspace, workspace_bytes, stream);
 }
@@ -116,7 +117,6 @@ sv_status spec_verify_tree_greedy(const void *target_logits, sv_dtype dtype, con
         !workspace)
         return SV_ERR_INVALID_ARG;
     if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
-    if (workspace_bytes < sv_workspace_bytes_tree(B, N, V)) return SV_ERR_WORKSPACE_TOO_SMALL;
     return run_greedy(target_logits, dtype, node_tokens, parents, B, N, V, true, out_tokens, out_accept_len,
                       out_status, out_path_nodes, workspace, workspace_bytes, stream);
 }
@@ -144,7 +144,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     WorkspaceLayout L;
     int32_t Ct, Cd, nt;
     sample_layout(B, gamma, Vt, Vd, target_dtype, draft_dtype, topp, &L, &Ct, &Cd, &nt);
-    if (workspace_bytes < L.total) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace_fits(workspace_bytes, L.counter_bytes, L.data_bytes)) return SV_ERR_WORKSPACE_TOO_SMALL;
     const int64_t NR = 2 * (int64_t)gamma + 1;
     if (!grid_fits((int64_t)B * (topp ? NR : ((int64_t)(gamma + 1) * Ct + (int64_t)gamma * Cd))) ||
         !grid_fits((int64_t)B * nt))
@@ -174,13 +174,14 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.out_p = out_p_tok;
     a.out_q = out_q_tok;
     char *base = static_cast<char *>(workspace);
+    char *data = base + counter_region(workspace_bytes);
     a.cnt_stats = reinterpret_cast<uint32_t *>(base + L.cnt_stats);
     a.cnt_draw = reinterpret_cast<uint32_t *>(base + L.cnt_draw);
-    a.seq = reinterpret_cast<SeqState *>(base + L.seq);
-    a.rows = reinterpret_cast<RowDesc *>(base + L.rows);
-    a.part = reinterpret_cast<MaxSum *>(base + L.part);
-    a.kept = reinterpret_cast<KeptEnt *>(base + L.kept);
-    a.tile_mass = reinterpret_cast<float *>(base + L.tile_mass);
+    a.seq = reinterpret_cast<SeqState *>(data + L.seq);
+    a.rows = reinterpret_cast<RowDesc *>(data + L.rows);
+    a.part = reinterpret_cast<MaxSum *>(data + L.part);
+    a.kept = reinterpret_cast<KeptEnt *>(data + L.kept);
+    a.tile_mass = reinterpret_cast<float *>(data + L.tile_mass);
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

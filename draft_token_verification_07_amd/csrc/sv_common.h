@@ -10,7 +10,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/spec_verify.h"
+#include "spec_verify.h"
 
 namespace sv {
 
@@ -19,6 +19,11 @@ constexpr int kWave = 64;
 // A native 16-byte vector (the HIP uint4 struct is not accepted by the
 // nontemporal-load builtin).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 2^x on the hardware exp unit (v_exp_f32, about 1 ulp).  Results below the
+// smallest normal float32 (x < -126) flush to zero: such weights are below
+// 1.2e-38 of the row maximum's.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // Element decoding.  bfloat16 widens to float32 exactly (it is the high half).
@@ -164,7 +169,7 @@ struct MaxSum {
 __device__ __forceinline__ MaxSum maxsum_merge(MaxSum a, MaxSum b, float c) {
     if (b.m > a.m) { MaxSum t = a; a = b; b = t; }
     if (b.m == -INFINITY) return a;            // also covers a.m == b.m == -inf
-    a.s = a.s + b.s * exp2f((b.m - a.m) * c);
+    a.s = a.s + b.s * exp2_hw((b.m - a.m) * c);
     return a;
 }
 __device__ __forceinline__ MaxSum wave_maxsum(MaxSum a, float c) {
@@ -190,23 +195,85 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 }
 
 // ---------------------------------------------------------------------------
+// Publishing results between workgroups of one launch.
+//
+// On gfx942/gfx950 each XCD has its own L2, and a device-scope fence writes
+// back and invalidates the whole L2 -- thousands of workgroups doing that
+// serialise on it.  Instead, data that another workgroup will read in the
+// same launch is written and read with agent-scope atomic stores / loads
+// (coherent across XCDs without cache maintenance), and the fences only
+// order: every thread waits for its own stores to complete (s_waitcnt
+// vmcnt(0)) before the workgroup bumps the counter, and the last workgroup
+// issues its loads only after it has seen the counter.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void pub_u32(void *p, uint32_t v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void pub_u64(void *p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sub_u32(const void *p) {
+    return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t sub_u64(const void *p) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Publish / read a trivially copyable struct whose size is a multiple of 8.
+template <typename T>
+__device__ __forceinline__ void pub(T *dst, const T &v) {
+    static_assert(sizeof(T) % 8 == 0, "published structs are whole 64-bit words");
+    uint64_t w[sizeof(T) / 8];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 8); ++k) pub_u64(reinterpret_cast<uint64_t *>(dst) + k, w[k]);
+}
+template <typename T>
+__device__ __forceinline__ T sub(const T *src) {
+    static_assert(sizeof(T) % 8 == 0, "published structs are whole 64-bit words");
+    uint64_t w[sizeof(T) / 8];
+#pragma unroll
+    for (int k = 0; k < (int)(sizeof(T) / 8); ++k) w[k] = sub_u64(reinterpret_cast<const uint64_t *>(src) + k);
+    T v;
+    __builtin_memcpy(&v, w, sizeof(T));
+    return v;
+}
+
+// Wait until this thread's vector-memory operations have completed
+// (s_waitcnt with vmcnt = 0, expcnt and lgkmcnt left at their maxima),
+// with a workgroup-scope fence so the compiler keeps the order.
+__device__ __forceinline__ void order_release() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+}
+__device__ __forceinline__ void order_acquire() {
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------
 // Last-arriving workgroup.  Every workgroup of a group publishes its partial
-// results, fences them to device scope, then bumps the group's counter; the
-// workgroup that brings the counter to `total` continues with the group's
-// combine step and returns the counter to zero for the next call.
+// results (pub*), then bumps the group's counter; the workgroup that brings
+// the counter to `total` continues with the group's combine step (reading
+// with sub*) and returns the counter to zero for the next call.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t total, int *flag_smem) {
-    __threadfence();
+    order_release();
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t prev = atomicAdd(counter, 1u);
-        int last = (prev == total - 1u);
-        if (last) atomicExch(counter, 0u);
+        const uint32_t prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (prev == total - 1u);
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *flag_smem = last;
     }
     __syncthreads();
     const bool last = *flag_smem != 0;
-    if (last) __threadfence();
+    if (last) {
+        order_acquire();
+        // the combine step is short and on the critical path: issue ahead of
+        // the streaming waves of other workgroups on this CU
+        __builtin_amdgcn_s_setprio(3);
+    }
     return last;
 }
 

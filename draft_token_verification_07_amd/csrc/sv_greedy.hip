@@ -25,7 +25,8 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     __shared__ ArgMax red[NT / kWave];
     __shared__ int last_flag;
     __shared__ int32_t s_n, s_status;
-    // epilogue scratch, sized by the launch: gmax[R] int32, then (tree) depth[R] int16, acc[R] uint8
+    // epilogue scratch, sized by the launch: gmax[R] int32, then (tree) tok[R],
+    // par[R] int32, depth[R] int16, acc[R] uint8
     extern __shared__ int32_t gmax[];
 
     const int32_t R = a.rows_per_seq, C = a.chunks;
@@ -35,25 +36,67 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     const int32_t b = row / R;
 
     // ---- stream one chunk of one row -----------------------------------
+    // Per lane: the running maximum over each iteration's U vectors costs one
+    // max3 per two elements; the index is recovered only when a lane's
+    // maximum improves (rare after the first iterations).  Indices rise per
+    // lane, so a strict '>' keeps the lowest index among equal values.
+    using E = Elem<DT>;
     const void *rowp = reinterpret_cast<const char *>(a.logits) +
-                       (size_t)row * (size_t)a.V * Elem<DT>::kBytes;
+                       (size_t)row * (size_t)a.V * E::kBytes;
     const RowSplit s = row_split<DT>(rowp, a.V);
     const int32_t lo = (int32_t)(((int64_t)s.nvec * c) / C);
     const int32_t hi = (int32_t)(((int64_t)s.nvec * (c + 1)) / C);
     ArgMax best;
     best.v = -INFINITY;
     best.i = INT32_MAX;
-    stream_row<DT, U, NT>(rowp, s, lo, hi, c == 0, c == C - 1, [&](float v, int32_t i) {
-        // indices rise per lane, so a strict '>' keeps the lowest index
+    auto one = [&](float v, int32_t i) {
         if (v > best.v) { best.v = v; best.i = i; }
-    });
+    };
+    const int tid = threadIdx.x;
+    if (c == 0 && tid < s.head) one(E::load(rowp, tid), tid);
+    const u32x4 *body = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(rowp) +
+                                                        (size_t)s.head * E::kBytes);
+    int32_t v = lo + tid;
+    for (; v + (U - 1) * NT < hi; v += U * NT) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[v + u * NT]);
+        float x[U][E::kPerVec];
+#pragma unroll
+        for (int u = 0; u < U; ++u) E::unpack(raw[u], x[u]);
+        float tm = x[0][0];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) tm = fmaxf(tm, x[u][k]);
+        if (tm > best.v) {
+            int32_t idx = INT32_MAX;
+#pragma unroll
+            for (int u = U - 1; u >= 0; --u)
+#pragma unroll
+                for (int k = E::kPerVec - 1; k >= 0; --k)
+                    if (x[u][k] == tm) idx = s.head + (v + u * NT) * E::kPerVec + k;
+            best.v = tm;
+            best.i = idx;
+        }
+    }
+    for (; v < hi; v += NT) {
+        float x[E::kPerVec];
+        E::unpack(__builtin_nontemporal_load(&body[v]), x);
+#pragma unroll
+        for (int k = 0; k < E::kPerVec; ++k) one(x[k], s.head + v * E::kPerVec + k);
+    }
+    if (c == C - 1 && tid < s.tail) {
+        const int32_t i = s.head + s.nvec * E::kPerVec + tid;
+        one(E::load(rowp, i), i);
+    }
     best = wave_argmax(best);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = best;
     __syncthreads();
     if (threadIdx.x == 0) {
         ArgMax r0 = red[0];
         for (int w = 1; w < NT / kWave; ++w) r0 = argmax_merge(r0, red[w]);
-        a.part[(size_t)row * C + c] = r0;
+        pub(&a.part[(size_t)row * C + c], r0);
     }
 
     // ---- last workgroup of the sequence: combine and walk ----------------
@@ -63,8 +106,8 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     __syncthreads();
     for (int32_t r = threadIdx.x; r < R; r += NT) {
         const ArgMax *p = a.part + ((size_t)b * R + r) * C;
-        ArgMax m = p[0];
-        for (int32_t k = 1; k < C; ++k) m = argmax_merge(m, p[k]);
+        ArgMax m = sub(&p[0]);
+        for (int32_t k = 1; k < C; ++k) m = argmax_merge(m, sub(&p[k]));
         // a row of -inf everywhere: the lowest id attaining the maximum is 0
         if (m.i == INT32_MAX) m.i = 0;
         if (!(m.v > -INFINITY) || m.v == INFINITY) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
@@ -76,14 +119,13 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
         // chain: x_i are the draft tokens, i < gamma = R - 1
         const int32_t g = R - 1;
         const int32_t *x = a.tokens + (size_t)b * g;
-        if (threadIdx.x == 0) {
-            int32_t n = g;
-            for (int32_t i = 0; i < g; ++i)
-                if (x[i] != gmax[i]) { n = i; break; }
-            s_n = n;
+        if (threadIdx.x == 0) s_n = g;
+        __syncthreads();
+        for (int32_t i = threadIdx.x; i < g; i += NT) {
+            const int32_t xi = x[i];
+            if (xi < 0 || xi >= a.V) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
+            if (xi != gmax[i]) atomicMin(&s_n, i);        // first mismatch
         }
-        for (int32_t i = threadIdx.x; i < g; i += NT)
-            if (x[i] < 0 || x[i] >= a.V) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
         __syncthreads();
         const int32_t n = s_n;
         for (int32_t i = threadIdx.x; i <= g; i += NT)
@@ -97,14 +139,19 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
 
     // tree: node k >= 1 has parent par[k] < k and token tok[k]
     const int32_t N = R;
-    const int32_t *tok = a.tokens + (size_t)b * N;
-    const int32_t *par = a.parents + (size_t)b * N;
-    int16_t *depth = reinterpret_cast<int16_t *>(gmax + N);
+    // tokens and parents are staged in LDS so the serial walk below never
+    // waits on global memory
+    int32_t *tok = gmax + N;
+    int32_t *par = tok + N;
+    int16_t *depth = reinterpret_cast<int16_t *>(par + N);
     uint8_t *acc = reinterpret_cast<uint8_t *>(depth + N);
-    for (int32_t k = 1 + threadIdx.x; k < N; k += NT) {
-        if (tok[k] < 0 || tok[k] >= a.V) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
-        if (par[k] < 0 || par[k] >= k) atomicOr(&s_status, (int)SV_SEQ_BAD_PARENT);
+    for (int32_t k = threadIdx.x; k < N; k += NT) {
+        tok[k] = a.tokens[(size_t)b * N + k];
+        par[k] = a.parents[(size_t)b * N + k];
+        if (k >= 1 && (tok[k] < 0 || tok[k] >= a.V)) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
+        if (k >= 1 && (par[k] < 0 || par[k] >= k)) atomicOr(&s_status, (int)SV_SEQ_BAD_PARENT);
     }
+    __syncthreads();
     if (threadIdx.x == 0) {
         // parents precede children, so one pass in index order settles every node
         acc[0] = 1;
@@ -143,7 +190,7 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
 template <int DT>
 static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st) {
     const size_t R = (size_t)a.rows_per_seq;
-    const size_t lds = R * sizeof(int32_t) + (a.tree ? R * (sizeof(int16_t) + sizeof(uint8_t)) : 0);
+    const size_t lds = R * sizeof(int32_t) + (a.tree ? R * (2 * sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
     hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll>), dim3(grid),
                        dim3(kGreedyThreads), lds, st, a);
     return hipGetLastError();

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/spec_verify.h"
+#include "spec_verify.h"
 
 namespace sv {
 
@@ -23,7 +23,7 @@ struct MaxSum;
 #define SV_GREEDY_UNROLL 4
 #endif
 #ifndef SV_GREEDY_ITERS
-#define SV_GREEDY_ITERS 4
+#define SV_GREEDY_ITERS 16
 #endif
 #ifndef SV_STATS_THREADS
 #define SV_STATS_THREADS 256
@@ -52,14 +52,17 @@ constexpr int kToppUnroll = SV_TOPP_UNROLL;
 constexpr int kSampThreads = 256;                   // residual / bonus draw
 constexpr int kMaxChunks = 4096;
 
-// Top-p candidate band: during streaming a token is kept in LDS when its
-// logit is within kToppBandNats * T of the running row maximum (so
-// y = z / T is within kToppBandNats of max y).  At the end the band is
-// verified to hold more than top_p of the row's mass; otherwise the row
-// takes the exact radix-select path over the whole row.
-constexpr float kToppBandNats = 9.0f;
-constexpr int kCandCap = 4096;      // LDS candidate slots per row (power of two)
-constexpr int kKeptCap = 4096;      // kept-list entries stored per row
+// Top-p band: during streaming a 16-byte vector is copied to LDS when its
+// largest logit is within kToppBandNats * T of the running row maximum (so
+// y = z / T is within kToppBandNats of max y); afterwards the band is the set
+// of tokens within that distance of the final maximum.  The band is checked
+// to hold more than top_p of the row's mass; otherwise the row takes the
+// exact radix-select path over the whole row.
+constexpr float kToppBandNats = 8.0f;
+constexpr int kCandCap = 2048;      // LDS slots for band tokens per row
+constexpr int kCandVecCap = 1024;   // LDS slots for band vectors (16 bytes each) per row
+constexpr int kKeptCap = 2048;      // kept-list entries stored per row
+constexpr int kQListCap = 1024;     // q lists up to this size are matched in LDS during a draw
 constexpr int kTile = 4096;         // target ids per residual/bonus tile
 
 // ---------------------------------------------------------------------------
@@ -96,7 +99,7 @@ struct RowDesc {
     int32_t tie_cut;
     int32_t nkept;    // kept ids; the list is stored iff nkept <= kKeptCap
     int32_t flags;    // RD_* bits
-    int32_t pad;
+    float ptok;       // p (or q) of the row's draft token; 0 for the bonus row
 };
 enum { RD_NO_MASS = 1, RD_HAS_LIST = 2, RD_FALLBACK = 4 };
 
@@ -135,8 +138,27 @@ struct SampleArgs {
     float *tile_mass;          // [B, ntiles]
 };
 
+// Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,
+// with K = counter_region(W) -- a function of W alone.  Every call returns
+// its counters to zero, and no call ever writes data below K, so calls of any
+// entry point and any size can share one workspace as long as they pass the
+// same W (the memory is zeroed once when allocated).
+inline size_t counter_region(size_t W) { return (W / 8) & ~(size_t)255; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Smallest W (a multiple of 256) that fits counter_bytes below K and
+// data_bytes above it.
+inline size_t workspace_need(size_t counter_bytes, size_t data_bytes) {
+    size_t W = align256(8 * counter_bytes + data_bytes + data_bytes / 4 + 4096);
+    while (counter_region(W) < counter_bytes || W - counter_region(W) < data_bytes) W += 256;
+    return W;
+}
+inline bool workspace_fits(size_t W, size_t counter_bytes, size_t data_bytes) {
+    return counter_region(W) >= counter_bytes && W - counter_region(W) >= data_bytes;
+}
+
 struct WorkspaceLayout {
-    size_t cnt_stats, cnt_draw, seq, rows, part, kept, tile_mass, total;
+    size_t cnt_stats, cnt_draw, counter_bytes;               // offsets from 0
+    size_t seq, rows, part, kept, tile_mass, data_bytes;     // offsets from K
 };
 bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int dt_t, int dt_d, bool topp,
                    WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *ntiles);

@@ -77,7 +77,10 @@ def gumbel_draw(rng: np.random.Generator, logits_f32: np.ndarray, temperature: f
 
 
 def _other_id(rng, V, avoid):
-    """A uniform id in [0, V) different from `avoid` (element-wise)."""
+    """A uniform id in [0, V) different from `avoid` (element-wise); with
+    V = 1 there is no other id and `avoid` itself is returned."""
+    if V == 1:
+        return np.zeros(np.shape(avoid), np.int32)
     r = rng.integers(0, V - 1, size=np.shape(avoid))
     return (r + (r >= avoid)).astype(np.int32)
 

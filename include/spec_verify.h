@@ -47,11 +47,15 @@
  *     the ABI.
  *   - Device-detected per-sequence conditions are reported in out_status[b]
  *     (when out_status is not NULL) as SV_SEQ_* bits; the call still completes.
- *   - The workspace is caller memory of at least sv_workspace_bytes_*() bytes
- *     that must be ZEROED ONCE when allocated.  Every call returns its
- *     counters to zero, so the same workspace serves later calls on the same
- *     stream.  Calls that may run concurrently need separate workspaces.
- *     After a call that failed on the device, zero the workspace again.
+ *   - The workspace is caller memory of workspace_bytes >=
+ *     sv_workspace_bytes_*() bytes that must be ZEROED ONCE when allocated.
+ *     Its first part (a fixed fraction of workspace_bytes) holds per-sequence
+ *     arrival counters that every call returns to zero; the rest holds
+ *     scratch data.  So one workspace serves later calls of every entry point
+ *     and every size on the same stream, provided each call passes the same
+ *     workspace_bytes (zero it again before passing a different value).
+ *     Calls that may run concurrently need separate workspaces.  After a
+ *     call that failed on the device, zero the workspace again.
  *   - Inputs containing NaN are outside the contract; -inf logits (masked
  *     tokens) are allowed.
  */

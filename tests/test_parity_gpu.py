@@ -33,7 +33,8 @@ def _gpu(oracle_mod):
 # greedy chain
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,gamma,V", [(16, 6, 100003), (7, 3, 4099), (5, 0, 777), (3, 2, 1), (2, 9, 65537)])
+@pytest.mark.parametrize("B,gamma,V", [(16, 6, 100003), (7, 3, 4099), (5, 0, 777), (3, 2, 1), (2, 9, 65537),
+                                       (4, 2, 2), (3, 1, 9)])
 def test_greedy_small(oracle_mod, B, gamma, V):
     _say("greedy", B, gamma, V)
     w = synth.greedy(100 + V, B=B, gamma=gamma, V=V)
@@ -154,6 +155,23 @@ def test_sample_topp_flat_rows_exact_path(oracle_mod):
     _check_sample(oracle_mod, w, "top-p flat")
 
 
+def test_sample_topp_wide_band(oracle_mod):
+    """About 1500 tokens within one nat of the maximum hold nearly all the
+    mass: the band is too wide for the pairwise select (radix path) and the
+    kept list too long for one entry per thread (sorted draw)."""
+    rng = np.random.default_rng(44)
+    B, g, V = 4, 2, 20008
+    zt = np.full((B, g + 1, V), -20.0, np.float32) + rng.standard_normal((B, g + 1, V)).astype(np.float32)
+    zt[:, :, 1000:2500] = 10.0 + rng.uniform(-0.5, 0.5, (B, g + 1, 1500)).astype(np.float32)
+    zd = (zt[:, :g] + rng.standard_normal((B, g, V)).astype(np.float32) * 0.05).astype(np.float32)
+    tok = rng.integers(1000, 2500, (B, g)).astype(np.int32)
+    for dt in ("bf16", "f32"):
+        cv = synth.bf16_bits if dt == "bf16" else (lambda x: x)
+        w = dict(target=cv(zt), draft=cv(zd), tokens=tok, u_accept=synth.uniforms(rng, (B, g)),
+                 u_sample=synth.uniforms(rng, (B,)), d2t=None, temperature=1.0, top_p=0.9)
+        _check_sample(oracle_mod, w, "top-p wide band " + dt)
+
+
 def test_sample_topp_ties_at_cutoff(oracle_mod):
     """Logits from a small set of values: the top-p cutoff falls inside a tie
     group in most rows, which the lowest-id-first order must split."""
@@ -181,8 +199,11 @@ def test_sample_equal_rows_accept_all(oracle_mod):
     """q == p: every draft is accepted whatever the uniforms (the target and
     draft rows are the same bits, so p and q come out the same bits)."""
     for top_p in (1.0, 0.9):
-        w = synth.sample_topp(61, B=12, gamma=4, V=20011)
+        w = synth.sample_topp(61, B=12, gamma=4, V=20008)   # rows share 16-byte alignment
         w["draft"] = w["target"][:, :4].copy()
+        # tokens inside the kept set (the row argmax is always kept); outside
+        # it p = q = 0 and the rule rejects
+        w["tokens"] = np.argmax(synth.bf16_to_f32(w["draft"]), axis=-1).astype(np.int32)
         w["u_accept"][:] = np.float32(1.0 - 2.0 ** -24)
         w["top_p"] = top_p
         g = run_sample(w)
@@ -226,6 +247,30 @@ def test_sample_status_bits(oracle_mod):
     _check_sample(oracle_mod, w, "status")
 
 
+def test_workspace_shared_across_entry_points_and_sizes(oracle_mod):
+    """One zeroed workspace, sized for the largest call, serves greedy, tree
+    and sampling calls of different batch sizes in any order (the counters
+    sit below a bound that depends on the workspace size alone)."""
+    import torch
+    import draft_token_verification_07_amd as sv
+    need = max(sv.sv_workspace_bytes_sample(40, 5, 30011, 30011, 0.9), sv.sv_workspace_bytes_sample(40, 5, 30011, 30011, 1.0),
+               sv.sv_workspace_bytes_greedy(40, 6, 30011), sv.sv_workspace_bytes_tree(40, 32, 30011))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for B in (40, 3, 17):
+            g = synth.greedy(900 + B, B=B, gamma=6, V=30011)
+            assert_same(run_greedy(g, ws=ws), oracle_mod.verify_greedy(g["target"], g["tokens"]),
+                        ["tokens", "accept_len", "status"])
+            t = synth.tree(910 + B, B=B, N=32, V=30011)
+            assert_same(run_tree(t, ws=ws), oracle_mod.verify_tree_greedy(t["target"], t["tokens"], t["parents"]),
+                        ["path", "tokens", "accept_len", "status"])
+            for top_p in (1.0, 0.9):
+                w = synth.sample_topp(920 + B, B=B, gamma=5, V=30011)
+                w["top_p"] = top_p
+                s = compare_sample(w, run_sample(w, ws=ws), oracle_mod)
+                assert s["boundary"] <= 1
+
+
 def test_sample_reproducible_and_workspace_reuse(oracle_mod):
     import torch
     import draft_token_verification_07_amd as sv
@@ -238,7 +283,8 @@ def test_sample_reproducible_and_workspace_reuse(oracle_mod):
         b = run_sample(w, ws=ws)
         for k in a:
             np.testing.assert_array_equal(a[k], b[k])
-        assert int(ws[:256].sum().item()) == 0          # counters back at zero
+        K = (need // 8) & ~255                          # the counter region of this workspace size
+        assert int(ws[:K].sum().item()) == 0            # counters back at zero
 
 
 # ---------------------------------------------------------------------------
