@@ -8,10 +8,18 @@ the headline metric is quoted on).  Inputs rotate over several copies in HBM
 (more than three times the 256 MB Infinity Cache in total) so every step reads
 its logits from HBM, not from the cache.
 
+Timing: after the warmup steps, the K timed steps are queued behind a short
+GPU sleep (so the host is ahead and the steps run back to back) and timed with
+one pair of HIP events on the launch stream; that gives `value` and
+`ms_per_step`.  The same K steps are then run once more with an event pair
+around every launch, which gives the mean launch duration used for the
+roofline (events between launches add a gap of a few microseconds each, so
+they are kept out of the throughput lap).
+
 Prints ONE JSON line: verified vocab rows/s (target + draft rows per second),
 the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
-launch time from HIP events on the launch stream, against 8 TB/s), and the
-CPU oracle timed on a bounded sample of the same workload.
+launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -100,33 +108,42 @@ def device_sets(w, nrot, dev):
     return sets
 
 
-def cpu_baseline(w, max_seqs: int):
+def cpu_baseline(w, max_seqs: int, work_seconds: float):
     """Time the oracle as it stands on the first max_seqs sequences, with
-    every host core this process may use."""
+    every host core this process may use, repeating the pass until about
+    work_seconds of CPU time (wall time x threads used) have been spent."""
     import oracle
     oracle.build(force=False)
     cores = min(len(os.sched_getaffinity(0)), 64)
     B = w["target"].shape[0]
     s = min(B, max_seqs)
     sl = slice(0, s)
+
+    def one_pass():
+        if w["kind"] == "sample":
+            oracle.verify_sample(w["target"][sl], w["draft"][sl], w["tokens"][sl], w["u_accept"][sl],
+                                 w["u_sample"][sl], w["temperature"], w["top_p"], d2t=w.get("d2t"),
+                                 nthreads=cores)
+            return s * (2 * w["tokens"].shape[1] + 1), min(cores, s)
+        if w["kind"] == "greedy":
+            oracle.verify_greedy(w["target"][sl], w["tokens"][sl])
+        else:
+            oracle.verify_tree_greedy(w["target"][sl], w["tokens"][sl], w["parents"][sl])
+        return s * w["target"].shape[1], 1
+
+    rows = passes = 0
+    used = 1
     t0 = time.perf_counter()
-    if w["kind"] == "sample":
-        oracle.verify_sample(w["target"][sl], w["draft"][sl], w["tokens"][sl], w["u_accept"][sl],
-                             w["u_sample"][sl], w["temperature"], w["top_p"], d2t=w.get("d2t"),
-                             nthreads=cores)
-        rows = s * (2 * w["tokens"].shape[1] + 1)
-        used = min(cores, s)
-    elif w["kind"] == "greedy":
-        oracle.verify_greedy(w["target"][sl], w["tokens"][sl])
-        rows = s * w["target"].shape[1]
-        used = 1
-    else:
-        oracle.verify_tree_greedy(w["target"][sl], w["tokens"][sl], w["parents"][sl])
-        rows = s * w["target"].shape[1]
-        used = 1
-    dt = time.perf_counter() - t0
+    while True:
+        r, used = one_pass()
+        rows += r
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt * used >= work_seconds or dt >= 3.0 * work_seconds:
+            break
     return dict(value=rows / dt, unit="rows/s", cores=used, kind="oracle",
-                sample="first %d of %d sequences of the same workload, %.2f s wall" % (s, B, dt))
+                sample="%d pass(es) over the first %d of %d sequences of the same workload, %.2f s wall"
+                       % (passes, s, B, dt))
 
 
 def main():
@@ -140,13 +157,15 @@ def main():
                     help="total bytes of rotated input copies (> 3x the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=64)
+    ap.add_argument("--cpu-work-seconds", type=float, default=10.0,
+                    help="CPU time (wall x threads) to spend timing the oracle")
     ap.add_argument("--queue-ahead-cycles", type=float, default=4e7,
                     help="GPU sleep queued before the timed steps (lets the host run ahead)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="instead of the benchmark, copy this many bytes device-to-device "
                          "(a kernel of known traffic, to scale rocprofv3 byte counters)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM bytes per launch from rocprofv3 counters, if present")
+    ap.add_argument("--traffic-table", default=os.path.join(ROOT, "profiles", "hbm_traffic.md"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (markdown table)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -222,51 +241,56 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+    t0e = torch.cuda.Event(enable_timing=True)
+    t1e = torch.cuda.Event(enable_timing=True)
+
+    def queue_ahead():
+        # keep the GPU busy while the host queues the steps, so that they run
+        # back to back and the events time the GPU, not Python
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(args.queue_ahead_cycles))
+
+    # lap 1: throughput (no events between steps)
     torch.cuda.synchronize()
-    # keep the GPU busy while the host queues the timed steps, so that the
-    # steps run back to back and the events time the GPU, not Python
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(args.queue_ahead_cycles))
-    t_all0.record(stream)
+    queue_ahead()
+    t0e.record(stream)
+    for i in range(K):
+        step(sets[i % nrot])
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0e.elapsed_time(t1e)
+
+    # lap 2: per-launch durations of the same K steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    queue_ahead()
     for i in range(K):
         ev[i][0].record(stream)
         step(sets[i % nrot])
         ev[i][1].record(stream)
-    t_all1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_all0.elapsed_time(t_all1)
     per_launch_ms = [a.elapsed_time(b) for a, b in ev]
     mean_launch_ms = float(np.mean(per_launch_ms))
+
     ms_per_step = total_ms / K
     rows = rows_per_step(w)
     value = rows * K / (total_ms / 1e3)
     achieved = nbytes / (mean_launch_ms / 1e3) / 1e9
-
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            ent = tj.get(args.workload)
-            if ent and ent.get("kernel_sources_sha") == _sources_sha():
-                traffic = ent.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = read_traffic(args.traffic_table, args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, args.cpu_seqs)
+        cpu = cpu_baseline(w, args.cpu_seqs, args.cpu_work_seconds)
 
     dtype = "f32"
     cfg = dict(workload=args.workload, desc=WORKLOADS[args.workload]["desc"],
                logits_dtype=str(w["target"].dtype).replace("uint16", "bf16"),
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
-               kernel=kernel, step_ms_median=float(np.median(per_launch_ms)),
-               step_ms_p10=float(np.percentile(per_launch_ms, 10)),
-               step_ms_p90=float(np.percentile(per_launch_ms, 90)),
+               kernel=kernel, launch_ms_mean=mean_launch_ms,
+               launch_ms_median=float(np.median(per_launch_ms)),
+               launch_ms_p10=float(np.percentile(per_launch_ms, 10)),
+               launch_ms_p90=float(np.percentile(per_launch_ms, 90)),
+               step_GBps=float(nbytes / (ms_per_step / 1e3) / 1e9),
                seqs_per_s=float(w["target"].shape[0] * K / (total_ms / 1e3)))
     line = dict(metric=METRIC, value=value, unit="rows/s", n_gpus=1, steps=K, warmup=args.warmup,
                 ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None,
@@ -277,13 +301,34 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def _sources_sha():
+def sources_sha() -> str:
+    """Hash of the kernel sources, so counter readings of an older kernel are
+    not reported for a changed one."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "draft_token_verification_07_amd", "csrc")
     for f in sorted(os.listdir(d)):
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def read_traffic(path: str, workload: str):
+    """HBM bytes per launch for `workload` from the counter table, or None when
+    the table is absent or was measured on other kernel sources.  Rows look
+    like `| workload | sources | fetch KiB | write KiB | factor | bytes/launch |`."""
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    sha = sources_sha()
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] == workload and cells[1] == sha:
+            try:
+                return float(cells[5])
+            except ValueError:
+                return None
+    return None
 
 
 if __name__ == "__main__":
