@@ -84,8 +84,8 @@ size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t V
         Vd > SV_MAX_VOCAB || !(top_p > 0.0f))
         return 0;
     WorkspaceLayout L;
-    int32_t ct, cd, nt;
-    sample_layout(B, gamma, Vt, Vd, SV_BF16, SV_BF16, top_p < 1.0f, &L, &ct, &cd, &nt);
+    int32_t ct, cd, tl, nt;
+    sample_layout(B, gamma, Vt, Vd, 4, 4, top_p < 1.0f, &L, &ct, &cd, &tl, &nt);
     return workspace_need(L.counter_bytes, L.data_bytes);
 }
 
@@ -142,11 +142,11 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
 
     const bool topp = top_p < 1.0f;
     WorkspaceLayout L;
-    int32_t Ct, Cd, nt;
-    sample_layout(B, gamma, Vt, Vd, target_dtype, draft_dtype, topp, &L, &Ct, &Cd, &nt);
+    int32_t Ct, Cd, tl, nt;
+    sample_layout(B, gamma, Vt, Vd, esize(target_dtype), esize(draft_dtype), topp, &L, &Ct, &Cd, &tl, &nt);
     if (!workspace_fits(workspace_bytes, L.counter_bytes, L.data_bytes)) return SV_ERR_WORKSPACE_TOO_SMALL;
     const int64_t NR = 2 * (int64_t)gamma + 1;
-    if (!grid_fits((int64_t)B * (topp ? NR : ((int64_t)(gamma + 1) * Ct + (int64_t)gamma * Cd))) ||
+    if (!grid_fits((int64_t)B * (topp ? NR : (1 + (int64_t)(gamma + 1) * Ct + (int64_t)gamma * Cd))) ||
         !grid_fits((int64_t)B * nt))
         return SV_ERR_TOO_LARGE;
 
@@ -167,6 +167,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.topp = topp ? 1 : 0;
     a.Ct = Ct;
     a.Cd = Cd;
+    a.tile = tl;
     a.ntiles = nt;
     a.out_tokens = out_tokens;
     a.out_len = out_accept_len;
@@ -181,7 +182,10 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.rows = reinterpret_cast<RowDesc *>(data + L.rows);
     a.part = reinterpret_cast<MaxSum *>(data + L.part);
     a.kept = reinterpret_cast<KeptEnt *>(data + L.kept);
-    a.tile_mass = reinterpret_cast<float *>(data + L.tile_mass);
+    a.probe = reinterpret_cast<Probe *>(data + L.probe);
+    a.tile_mass = reinterpret_cast<uint64_t *>(data + L.tile_mass);
+    a.tile_jb = reinterpret_cast<int32_t *>(data + L.tile_jb);
+
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

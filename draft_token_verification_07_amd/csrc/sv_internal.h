@@ -63,7 +63,20 @@ constexpr int kCandCap = 2048;      // LDS slots for band tokens per row
 constexpr int kCandVecCap = 1024;   // LDS slots for band vectors (16 bytes each) per row
 constexpr int kKeptCap = 2048;      // kept-list entries stored per row
 constexpr int kQListCap = 1024;     // q lists up to this size are matched in LDS during a draw
-constexpr int kTile = 4096;         // target ids per residual/bonus tile
+constexpr int kTile = 4096;         // most target ids per residual/bonus tile
+constexpr int kTileMin = 1024;      // fewest (tiles shrink for small batches)
+constexpr int kDrawMinWgs = 512;    // tiles shrink until the draw has this many workgroups
+constexpr int kDrawGroup = 8;       // draw tiles per first-level arrival counter
+#ifndef SV_STATS_MIN_WGS
+#define SV_STATS_MIN_WGS 256
+#endif
+constexpr int kStatsMinWgs = SV_STATS_MIN_WGS;  // plain-mode chunks shrink until the grid has this many (small batches)
+constexpr int kStatsMinChunk = 2048;  // ... but never below this many elements per chunk
+#ifndef SV_STATS_CHUNK_BYTES
+#define SV_STATS_CHUNK_BYTES 131072
+#endif
+constexpr int kStatsChunkBytes = SV_STATS_CHUNK_BYTES;  // logits bytes per plain-mode chunk
+constexpr int kPartCap = 2048;      // chunk partials staged in LDS by a sequence epilogue
 
 // ---------------------------------------------------------------------------
 // Greedy / tree
@@ -108,10 +121,16 @@ struct KeptEnt {      // one kept id of a row and its weight w
     float w;
 };
 
+struct Probe {        // the logits at one draft token: target row, draft row
+    float zt;         // target logit of x_i (0 when x_i is out of range)
+    float zd;         // draft logit of x_i; -inf when x_i is off the d2t map
+};
+
 struct SeqState {     // written by the statistics epilogue for the draw kernel
     int32_t n;        // accepted drafts
     int32_t status;   // SV_SEQ_* bits
     int32_t pad0, pad1;
+    RowDesc dp, dq;   // the rows the draw uses: target row n, draft row n (= dp for the bonus)
 };
 
 struct SampleArgs {
@@ -125,17 +144,19 @@ struct SampleArgs {
     float T, c, top_p;         // c = log2(e) / T
     int32_t topp;              // top-p filter on
     int32_t Ct, Cd;            // chunks per target / draft row (1 with top-p)
-    int32_t ntiles;            // draw tiles per sequence (plain mode)
+    int32_t tile, ntiles;      // target ids per draw tile, draw tiles per row
     int32_t *out_tokens, *out_len, *out_status;
     float *out_p, *out_q;
     // workspace
     uint32_t *cnt_stats;       // [B]
-    uint32_t *cnt_draw;        // [B]
+    uint32_t *cnt_draw;        // [B, 1 + ceil(ntiles / kDrawGroup)]
     SeqState *seq;             // [B]
     RowDesc *rows;             // [B, 2*gamma+1]: target rows then draft rows
     MaxSum *part;              // [B, (gamma+1)*Ct + gamma*Cd]
     KeptEnt *kept;             // [B, 2*gamma+1, kKeptCap] (top-p only)
-    float *tile_mass;          // [B, ntiles]
+    Probe *probe;              // [B, gamma] (plain mode)
+    uint64_t *tile_mass;       // [B, ntiles] fixed-point draw masses (plain mode)
+    int32_t *tile_jb;          // [ntiles + 1] first draft id of each draw tile under d2t (plain mode)
 };
 
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,
@@ -158,11 +179,13 @@ inline bool workspace_fits(size_t W, size_t counter_bytes, size_t data_bytes) {
 
 struct WorkspaceLayout {
     size_t cnt_stats, cnt_draw, counter_bytes;               // offsets from 0
-    size_t seq, rows, part, kept, tile_mass, data_bytes;     // offsets from K
+    size_t seq, rows, part, kept, probe, tile_mass, tile_jb, data_bytes;   // offsets from K
 };
-bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int dt_t, int dt_d, bool topp,
-                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *ntiles);
-int32_t stats_chunks(int32_t V, int dtype);
+// Workspace layout and launch shape of one sampling call; bt / bd are the
+// element sizes of the target / draft logits.  4-byte elements give the
+// largest layout, which the workspace size query assumes.
+bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt, int32_t bd, bool topp,
+                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *tile, int32_t *ntiles);
 hipError_t launch_sample(const SampleArgs &a, int dt_t, int dt_d, hipStream_t st);
 
 }  // namespace sv

@@ -65,6 +65,21 @@ __device__ __forceinline__ float row_prob(const RowDesc &d, float z, int32_t j, 
     return exp2_hw((z - d.m) * c) / d.Zk;
 }
 
+// A descriptor read field by field (a whole-struct copy through a
+// conditional would be staged in private memory).
+__device__ __forceinline__ RowDesc load_desc(const RowDesc *p) {
+    RowDesc d;
+    d.m = p->m;
+    d.Z = p->Z;
+    d.Zk = p->Zk;
+    d.key = p->key;
+    d.tie_cut = p->tie_cut;
+    d.nkept = p->nkept;
+    d.flags = p->flags;
+    d.ptok = p->ptok;
+    return d;
+}
+
 __device__ __forceinline__ bool bad_max(float m) { return !(m > -INFINITY) || m == INFINITY; }
 
 template <int DT>
@@ -218,137 +233,260 @@ __device__ __forceinline__ int32_t wg_inverse_cdf(int32_t n, G &&get, double u, 
 }
 
 // ---------------------------------------------------------------------------
-// Draw from the residual (or bonus) distribution over target ids [t0, t1):
-// weights r_t = max(0, p_n(t) - q_n(t)) when resid, else p_n(t).
+// Draws over whole target rows (no kept list): the residual max(0, p_n - q_n),
+// or p itself, over the target ids in tiles.  A tile's weights are staged in
+// LDS in id order; each thread owns a contiguous segment of them; segment sums
+// (float64, in id order) are scanned in thread order, and the tile's mass is
+// that scan's total.  The pass that picks a tile and the pass that searches
+// inside it compute the same numbers the same way, so they agree bit for bit.
 // ---------------------------------------------------------------------------
 struct DrawCtx {
     const void *trow;          // target row n
-    const void *drow;          // draft row n (resid only)
-    const int32_t *d2t;
+    const void *drow;          // draft row n (residual only)
+    const int32_t *d2t;        // draft id -> target id, or null
     int32_t Vd;
     RowDesc dp, dq;
     float c;
     bool resid;
 };
 
-// Fills s_r[0, t1 - t0) with the weights (and s_q as scratch for d2t).
-template <int DTT, int DTD, int NT>
-__device__ __forceinline__ void tile_weights(const DrawCtx &x, int32_t t0, int32_t t1, float *s_r, float *s_q) {
-    const int32_t len = t1 - t0;
-    if (x.resid && x.d2t) {
-        for (int32_t k = threadIdx.x; k < len; k += NT) s_q[k] = 0.0f;
-        __syncthreads();
-        const int32_t j0 = lower_bound_i32(x.d2t, x.Vd, t0);
-        const int32_t j1 = lower_bound_i32(x.d2t, x.Vd, t1);
-        for (int32_t j = j0 + threadIdx.x; j < j1; j += NT) {
-            const int32_t t = x.d2t[j];
-            if (t >= t0 && t < t1) s_q[t - t0] = row_prob(x.dq, ld_logit<DTD>(x.drow, j), j, x.c);
+// First index in [0, n) whose value is >= t in the ascending array v, found
+// by one whole wave: 64 probes narrow the range 64-fold per round (three
+// dependent loads for 32000 entries, where a binary search takes fifteen).
+// All 64 lanes call it together and get the same value.
+__device__ __forceinline__ int32_t wave_lower_bound(const int32_t *v, int32_t n, int32_t t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int32_t lo = 0, hi = n;                       // the answer lies in [lo, hi]
+    while (hi - lo > kWave) {
+        const int32_t step = (hi - lo + kWave - 1) / kWave;
+        const int32_t i = lo + lane * step;
+        const int cnt = __popcll(__ballot(i < hi && v[i] < t));
+        if (cnt == 0) {
+            hi = lo;
+            break;
         }
-        __syncthreads();
+        const int32_t nlo = lo + (cnt - 1) * step + 1;
+        hi = min(hi, lo + cnt * step);
+        lo = nlo;
     }
-    for (int32_t k = threadIdx.x; k < len; k += NT) {
-        const int32_t t = t0 + k;
-        const float p = row_prob(x.dp, ld_logit<DTT>(x.trow, t), t, x.c);
-        float r = p;
-        if (x.resid) {
-            const float q = x.d2t ? s_q[k] : row_prob(x.dq, ld_logit<DTD>(x.drow, t), t, x.c);
-            r = p - q > 0.0f ? p - q : 0.0f;
-        }
-        s_r[k] = r;
-    }
-    __syncthreads();
+    const int32_t i = lo + lane;
+    return lo + __popcll(__ballot(i < hi && v[i] < t));
 }
 
-// Sum of a tile's weights: per-thread sums in index-stride order, then a
-// fixed-order tree.  Deterministic for a given launch shape.
-template <int DTT, int DTD, int NT>
-__device__ __forceinline__ float tile_mass(const DrawCtx &x, int32_t t0, int32_t t1, float *s_r, float *s_q,
-                           float *s_ftmp) {
-    tile_weights<DTT, DTD, NT>(x, t0, t1, s_r, s_q);
-    float acc = 0.0f;
-    for (int32_t k = threadIdx.x; k < t1 - t0; k += NT) acc += s_r[k];
-    return wg_sum_f32<NT>(acc, s_ftmp);
-}
-
-// Given the tile sums, find the token for u * S; returns -1 when S == 0.
-template <int DTT, int DTD, int NT>
-__device__ __forceinline__ int32_t draw_from_tiles(const DrawCtx &x, int32_t V, const float *mass, int32_t ntiles,
-                                   double u, float *s_r, float *s_q, double *s_dtmp,
-                                   int32_t *s_itmp, double *s_bcast) {
-    if (threadIdx.x == 0) {
-        double S = 0.0;
-        auto mt = [&](int32_t t) { return __uint_as_float(sub_u32(&mass[t])); };
-        for (int32_t t = 0; t < ntiles; ++t) S += (double)mt(t);
-        const double target = u * S;
-        double run = 0.0, before = 0.0;
-        int32_t tile = -1, lastpos = -1;
-        for (int32_t t = 0; t < ntiles; ++t) {
-            const float m_t = mt(t);
-            if (m_t > 0.0f) lastpos = t;
-            before = run;
-            run += (double)m_t;
-            if (run > target) { tile = t; break; }
-        }
-        if (tile < 0) { tile = lastpos; before = S - (lastpos >= 0 ? (double)mt(lastpos) : 0.0); }
-        s_bcast[0] = S;
-        s_bcast[1] = target - before;
-        s_bcast[2] = (double)tile;
-    }
-    __syncthreads();
-    const double S = s_bcast[0], tin = s_bcast[1];
-    const int32_t tile = (int32_t)s_bcast[2];
-    __syncthreads();
-    if (!(S > 0.0) || tile < 0) return -1;
-    const int32_t t0 = tile * kTile, t1 = min(V, t0 + kTile);
-    tile_weights<DTT, DTD, NT>(x, t0, t1, s_r, s_q);
-    double tot;
-    const int32_t k = wg_inverse_cdf<NT>(t1 - t0, [&](int32_t s) { return s_r[s]; }, tin, false,
-                                         s_dtmp, s_itmp, &tot);
-    return k < 0 ? -1 : t0 + k;
-}
-
-// ---------------------------------------------------------------------------
-// The accept chain (shared by both modes); runs in the last workgroup of a
-// sequence once every row descriptor of the sequence is in s_rows.
-// Returns n and writes p_tok / q_tok / the accepted tokens / padding / len /
-// status; the drawn token at position n is written by the caller.
-// ---------------------------------------------------------------------------
-template <int DTT, int DTD, int NT>
-__device__ __forceinline__ int32_t accept_chain(const SampleArgs &a, int32_t b, const RowDesc *s_rows,
-                                int32_t *s_itmp, int32_t *s_status) {
-    const int32_t g = a.gamma;
-    const int32_t *x = a.tokens + (size_t)b * g;
-    int32_t first_rej = INT32_MAX;
-    for (int32_t i = threadIdx.x; i < g; i += NT) {
-        const int32_t t = x[i];
-        float pa = 0.0f, qc = 0.0f;
-        if (t < 0 || t >= a.Vt) {
-            atomicOr(s_status, (int)SV_SEQ_TOKEN_RANGE);
-        } else {
-            const RowDesc dp = s_rows[i], dq = s_rows[g + 1 + i];
-            const void *trow = reinterpret_cast<const char *>(a.tl) +
-                               ((size_t)b * (g + 1) + i) * (size_t)a.Vt * Elem<DTT>::kBytes;
-            const void *drow = reinterpret_cast<const char *>(a.dl) +
-                               ((size_t)b * g + i) * (size_t)a.Vd * Elem<DTD>::kBytes;
-            pa = row_prob(dp, ld_logit<DTT>(trow, t), t, a.c);
-            if (a.d2t) {
-                const int32_t j = lower_bound_i32(a.d2t, a.Vd, t);
-                if (j < a.Vd && a.d2t[j] == t) qc = row_prob(dq, ld_logit<DTD>(drow, j), j, a.c);
+// The same search by groups of G consecutive lanes (G divides 64), each group
+// with its own t: G probes per round narrow a group's range G-fold, so one
+// wave runs 64 / G searches at once.  Every lane of a group returns the
+// group's answer; all 64 lanes call it together.
+template <int G>
+__device__ __forceinline__ int32_t group_lower_bound(const int32_t *v, int32_t n, int32_t t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gl = lane & (G - 1);
+    const uint64_t gmask = (G == kWave ? ~0ull : ((1ull << G) - 1ull)) << (lane & ~(G - 1));
+    int32_t lo = 0, hi = n;                       // the group's answer lies in [lo, hi]
+    while (__ballot(hi - lo > G)) {
+        const bool active = hi - lo > G;
+        const int32_t step = active ? (hi - lo + G - 1) / G : 0;
+        const int32_t i = lo + gl * step;
+        const int cnt = __popcll(__ballot(active && i < hi && v[i] < t) & gmask);
+        if (active) {
+            if (cnt == 0) {
+                hi = lo;
             } else {
-                qc = row_prob(dq, ld_logit<DTD>(drow, t), t, a.c);
+                const int32_t nlo = lo + (cnt - 1) * step + 1;
+                hi = min(hi, lo + cnt * step);
+                lo = nlo;
             }
         }
-        if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
-        if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
-        // u * q < p, exactly: both products fit a double
-        const double u = (double)a.u_acc[(size_t)b * g + i];
-        if (!(u * (double)qc < (double)pa) && i < first_rej) first_rej = i;
     }
-    const int32_t fr = wg_min_i32<NT>(first_rej, s_itmp);
-    const int32_t n = fr == INT32_MAX ? g : fr;
-    for (int32_t i = threadIdx.x; i <= g; i += NT)
-        if (i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? x[i] : -1;
-    return n;
+    const int32_t i = lo + gl;
+    return lo + __popcll(__ballot(i < hi && v[i] < t) & gmask);
+}
+
+// The draft ids whose d2t entries fall in target ids [t0, t1): [s_j[0], s_j[1]).
+// Waves 0 and 1 search in parallel (NT >= 128).
+template <int NT>
+__device__ __forceinline__ void tile_jrange(const DrawCtx &x, int32_t t0, int32_t t1, int32_t *s_j) {
+    static_assert(NT >= 2 * kWave, "two waves search the two ends");
+    const int w = threadIdx.x / kWave;
+    if (w < 2) {
+        const int32_t j = wave_lower_bound(x.d2t, x.Vd, w == 0 ? t0 : t1);
+        if ((threadIdx.x & (kWave - 1)) == 0) s_j[w] = j;
+    }
+    __syncthreads();
+}
+
+// Weights of target ids [t0, t0 + len) into s_w[0, len), len <= kTile.
+// [j0, j1) are the draft ids mapped into the tile (d2t residual only).  Every
+// load of the tile is issued before any is used (one round trip); the q
+// values of mapped ids are scattered into s_w, then each slot is overwritten
+// with its weight by the thread that reads it.
+template <int DTT, int DTD, int NT>
+__device__ __forceinline__ void tile_fill(const DrawCtx &x, int32_t t0, int32_t len, int32_t j0, int32_t j1,
+                                          float *s_w) {
+    constexpr int U = kTile / NT;
+    const bool scat = x.resid && x.d2t != nullptr && j1 > j0;
+    const bool dense_q = x.resid && x.d2t == nullptr;
+    // Loads are unconditional, at clamped indices (a load under a divergent
+    // branch is waited for inside it, one round trip each); out-of-range
+    // values are masked afterwards.  The branches below are uniform.
+    float z[U], zq[U];
+    int32_t jt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) z[u] = ld_logit<DTT>(x.trow, t0 + min(u * NT + (int32_t)threadIdx.x, len - 1));
+    if (dense_q) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) zq[u] = ld_logit<DTD>(x.drow, t0 + min(u * NT + (int32_t)threadIdx.x, len - 1));
+    } else if (scat) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = min(j0 + u * NT + (int32_t)threadIdx.x, j1 - 1);
+            jt[u] = x.d2t[j];
+            zq[u] = ld_logit<DTD>(x.drow, j);
+        }
+    }
+    if (scat) {
+        for (int32_t k = threadIdx.x; k < len; k += NT) s_w[k] = 0.0f;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = j0 + u * NT + (int32_t)threadIdx.x;
+            const int32_t k = jt[u] - t0;
+            if (j < j1 && (uint32_t)k < (uint32_t)len) s_w[k] = row_prob(x.dq, zq[u], j, x.c);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int32_t k = u * NT + (int32_t)threadIdx.x;
+        if (k < len) {
+            float r = row_prob(x.dp, z[u], t0 + k, x.c);
+            if (x.resid) {
+                // q: scattered from the mapped draft ids, or the same id's draft logit
+                const float q = scat ? s_w[k] : dense_q ? row_prob(x.dq, zq[u], t0 + k, x.c) : 0.0f;
+                r = r - q > 0.0f ? r - q : 0.0f;
+            }
+            s_w[k] = r;
+        }
+    }
+    __syncthreads();
+}
+
+// This thread's segment [*s0, *s1) of a filled tile and its float64 sum in id order.
+template <int NT>
+__device__ __forceinline__ double tile_seg(const float *s_w, int32_t len, int32_t *s0, int32_t *s1) {
+    const int32_t per = (len + NT - 1) / NT;
+    *s0 = min(len, (int32_t)threadIdx.x * per);
+    *s1 = min(len, *s0 + per);
+    double seg = 0.0;
+    for (int32_t s = *s0; s < *s1; ++s) seg += (double)s_w[s];
+    return seg;
+}
+
+// Exclusive (*lo) and inclusive (*hi) prefix of one float64 per thread, in
+// thread order, and the total.  hi of thread t equals lo of thread t + 1 bit
+// for bit, and hi of the last thread equals the total.
+template <int NT>
+__device__ __forceinline__ void wg_scan_f64(double v, double *s_tmp, double *lo, double *hi, double *total) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const double inc = wave_incl_scan(v);
+    double exc = __shfl_up(inc, 1, kWave);
+    if (lane == 0) exc = 0.0;
+    if (lane == kWave - 1) s_tmp[w] = inc;
+    __syncthreads();
+    double base = 0.0, tot = 0.0;
+    for (int k = 0; k < NT / kWave; ++k) {
+        if (k < w) base += s_tmp[k];
+        tot += s_tmp[k];
+    }
+    __syncthreads();
+    *lo = base + exc;
+    *hi = base + inc;
+    *total = tot;
+}
+
+// Mass of a filled tile (the same numbers tile_search scans).
+template <int NT>
+__device__ __forceinline__ double tile_total(const float *s_w, int32_t len, double *s_dtmp) {
+    int32_t s0, s1;
+    const double seg = tile_seg<NT>(s_w, len, &s0, &s1);
+    double lo, hi, tot;
+    wg_scan_f64<NT>(seg, s_dtmp, &lo, &hi, &tot);
+    return tot;
+}
+
+// Offset in a filled tile of the first id of positive weight whose inclusive
+// sum exceeds tin (0 <= tin < the tile's mass); the tile's last id of positive
+// weight when rounding leaves none; -1 when every weight is zero.
+template <int NT>
+__device__ __forceinline__ int32_t tile_search(const float *s_w, int32_t len, double tin, double *s_dtmp,
+                                               int32_t *s_itmp) {
+    int32_t s0, s1;
+    const double seg = tile_seg<NT>(s_w, len, &s0, &s1);
+    double lo, hi, tot;
+    wg_scan_f64<NT>(seg, s_dtmp, &lo, &hi, &tot);
+    int32_t found = INT32_MAX;
+    if (lo <= tin && tin < hi) {               // one thread's segment brackets tin
+        double run = lo;
+        int32_t lastpos = -1;
+        for (int32_t s = s0; s < s1; ++s) {
+            const float w = s_w[s];
+            if (w > 0.0f) {
+                lastpos = s;
+                run += (double)w;
+                if (run > tin) {
+                    found = s;
+                    break;
+                }
+            }
+        }
+        if (found == INT32_MAX) found = lastpos;
+    }
+    const int32_t f = wg_min_i32<NT>(found, s_itmp);
+    if (f != INT32_MAX) return f;
+    int32_t lp = -1;
+    for (int32_t s = s1 - 1; s >= s0; --s)
+        if (s_w[s] > 0.0f) {
+            lp = s;
+            break;
+        }
+    return wg_max_i32<NT>(lp, s_itmp);
+}
+
+// A whole draw in one workgroup (rare paths): one sweep over the tiles sums
+// the masses, a second finds the tile holding u * S and searches it.
+// Returns -1 when S == 0.
+template <int DTT, int DTD, int NT>
+__device__ SV_RARE int32_t draw_row_one_wg(const DrawCtx &x, int32_t Vt, int32_t tile, double u, float *s_w,
+                                           double *s_dtmp, int32_t *s_itmp, int32_t *s_j) {
+    auto fill = [&](int32_t t0, int32_t len) {
+        int32_t j0 = 0, j1 = 0;
+        if (x.resid && x.d2t) {
+            tile_jrange<NT>(x, t0, t0 + len, s_j);
+            j0 = s_j[0];
+            j1 = s_j[1];
+        }
+        tile_fill<DTT, DTD, NT>(x, t0, len, j0, j1, s_w);
+    };
+    double S = 0.0;
+    for (int32_t t0 = 0; t0 < Vt; t0 += tile) {
+        const int32_t len = min(tile, Vt - t0);
+        fill(t0, len);
+        S += tile_total<NT>(s_w, len, s_dtmp);
+    }
+    if (!(S > 0.0)) return -1;
+    const double target = u * S;                // < S for u < 1
+    double run = 0.0;
+    for (int32_t t0 = 0; t0 < Vt; t0 += tile) {
+        const int32_t len = min(tile, Vt - t0);
+        fill(t0, len);
+        const double m = tile_total<NT>(s_w, len, s_dtmp);
+        if (m > 0.0 && target < run + m) {
+            const int32_t k = tile_search<NT>(s_w, len, target - run, s_dtmp, s_itmp);
+            return k < 0 ? -1 : t0 + k;
+        }
+        run += m;
+    }
+    return -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1100,11 +1238,11 @@ __device__ __forceinline__ int32_t draw_from_list(const SampleArgs &a, int32_t b
 }
 
 // Draw over the whole target row n tile by tile (top-p rows whose kept set
-// is too large for a list); one workgroup, out of line (rarely taken).
+// is too large for a list); one workgroup (rarely taken).
 template <int DTT, int DTD, int NT>
-__device__ SV_RARE int32_t draw_full_row(const SampleArgs &a, int32_t b, int32_t n, RowDesc dp,
-                                                           RowDesc dq, double u, float *s_r, double *s_dtmp,
-                                                           int32_t *s_itmp, double *s_bcast) {
+__device__ SV_RARE int32_t draw_full_row(const SampleArgs &a, int32_t b, int32_t n, const RowDesc &dp,
+                                         const RowDesc &dq, double u, float *s_w, double *s_dtmp, int32_t *s_itmp,
+                                         int32_t *s_j) {
     const int32_t g = a.gamma;
     DrawCtx x;
     x.trow = reinterpret_cast<const char *>(a.tl) + ((size_t)b * (g + 1) + n) * (size_t)a.Vt * Elem<DTT>::kBytes;
@@ -1115,19 +1253,12 @@ __device__ SV_RARE int32_t draw_full_row(const SampleArgs &a, int32_t b, int32_t
     x.dp = dp;
     x.dq = dq;
     x.c = a.c;
-    float *s_q = s_r + kTile;
-    float *mass = a.tile_mass + (size_t)b * a.ntiles;
-    int32_t tok = -1;
-    for (int attempt = 0; attempt < 2 && tok < 0; ++attempt) {
-        x.resid = n < g && attempt == 0;
-        if (attempt == 1 && !(n < g)) break;
-        for (int32_t t = 0; t < a.ntiles; ++t) {
-            const float mt = tile_mass<DTT, DTD, NT>(x, t * kTile, min(a.Vt, (t + 1) * kTile), s_r, s_q,
-                                                     reinterpret_cast<float *>(s_dtmp));
-            if (threadIdx.x == 0) pub_u32(&mass[t], __float_as_uint(mt));
-        }
-        __syncthreads();
-        tok = draw_from_tiles<DTT, DTD, NT>(x, a.Vt, mass, a.ntiles, u, s_r, s_q, s_dtmp, s_itmp, s_bcast);
+    x.resid = n < g;
+    int32_t tok = draw_row_one_wg<DTT, DTD, NT>(x, a.Vt, a.tile, u, s_w, s_dtmp, s_itmp, s_j);
+    if (tok < 0 && x.resid) {
+        // zero residual mass: draw from p_n itself
+        x.resid = false;
+        tok = draw_row_one_wg<DTT, DTD, NT>(x, a.Vt, a.tile, u, s_w, s_dtmp, s_itmp, s_j);
     }
     return tok;
 }
@@ -1145,12 +1276,12 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     static_assert(sizeof(RowDesc) * (2 * SV_MAX_GAMMA + 1) <= sizeof(uint64_t) * 4096,
                   "row descriptors must fit the band area");
     static_assert(sizeof(uint64_t) * kKeptCap <= sizeof(uint64_t) * 4096, "list sort must fit the band area");
-    static_assert(2 * kTile * sizeof(float) <= sizeof(uint64_t) * 4096, "draw tiles must fit the band area");
+    static_assert(kTile * sizeof(float) <= sizeof(uint64_t) * 4096, "draw tiles must fit the band area");
     __shared__ int last_flag;
     __shared__ int32_t s_itmp[NT / kWave];
     __shared__ double s_dtmp[NT / kWave];
     __shared__ int32_t s_status;
-    __shared__ double s_bcast[4];
+    __shared__ int32_t s_j[2];
 
     const int32_t g = a.gamma, NR = 2 * g + 1;
     const int32_t b = blockIdx.x / NR, r = blockIdx.x % NR;
@@ -1217,7 +1348,7 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     } else {
         // kept set too large for a list: tile-by-tile over the whole row
         tok = draw_full_row<DTT, DTD, NT>(a, b, n, dp, dq, u, reinterpret_cast<float *>(s_cand), s_dtmp, s_itmp,
-                                          s_bcast);
+                                          s_j);
     }
     if (threadIdx.x == 0) {
         a.out_tokens[(size_t)b * (g + 1) + n] = tok;
@@ -1244,11 +1375,23 @@ __device__ __forceinline__ MaxSum chunk_maxsum(const void *row, int32_t L, int32
     if (chunk == 0 && threadIdx.x < sp.head) one(E::load(row, threadIdx.x));
     const u32x4 *body = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(row) +
                                                         (size_t)sp.head * E::kBytes);
-    int32_t v = lo + threadIdx.x;
-    for (; v + (U - 1) * NT < hi; v += U * NT) {
+    // U vectors per lane per round, all loaded before any is used.  The loads
+    // are unconditional (past the chunk they repeat its last vector, and the
+    // values are masked to -inf afterwards): a load under a branch would be
+    // waited for inside the branch, one round trip per vector.
+    for (int32_t v = lo + threadIdx.x; v < hi; v += U * NT) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[min(v + u * NT, hi - 1)]);
         float xv[U][E::kPerVec];
 #pragma unroll
-        for (int u = 0; u < U; ++u) E::unpack(__builtin_nontemporal_load(&body[v + u * NT]), xv[u]);
+        for (int u = 0; u < U; ++u) {
+            E::unpack(raw[u], xv[u]);
+            if (v + u * NT >= hi) {
+#pragma unroll
+                for (int k = 0; k < E::kPerVec; ++k) xv[u][k] = -INFINITY;
+            }
+        }
         float tm = xv[0][0];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -1258,17 +1401,13 @@ __device__ __forceinline__ MaxSum chunk_maxsum(const void *row, int32_t L, int32
             s_l = (m_l == -INFINITY) ? 0.0f : s_l * exp2_hw((m_l - tm) * c);
             m_l = tm;
         }
-        const float mc = m_l * c;
+        if (m_l > -INFINITY) {
+            const float mc = m_l * c;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int k = 0; k < E::kPerVec; ++k) s_l += exp2_hw(fmaf(xv[u][k], c, -mc));
-    }
-    for (; v < hi; v += NT) {
-        float xv[E::kPerVec];
-        E::unpack(__builtin_nontemporal_load(&body[v]), xv);
-#pragma unroll
-        for (int k = 0; k < E::kPerVec; ++k) one(xv[k]);
+                for (int k = 0; k < E::kPerVec; ++k) s_l += exp2_hw(fmaf(xv[u][k], c, -mc));
+        }
     }
     if (chunk == C - 1 && threadIdx.x < sp.tail) one(E::load(row, sp.head + sp.nvec * E::kPerVec + threadIdx.x));
     MaxSum ms;
@@ -1289,9 +1428,76 @@ __device__ __forceinline__ MaxSum chunk_maxsum(const void *row, int32_t L, int32
     return tot;
 }
 
+// The logits at each draft token of sequence b (target row i at x_i, draft
+// row i at x_i's draft id), read while the chunk workgroups stream, so the
+// chain needs no loads of its own.  With d2t, groups of G lanes search the map
+// for the tokens' draft ids, 64 / G tokens per wave at once.
+template <int DTT, int DTD, int NT, int G>
+__device__ __forceinline__ void probe_tokens_g(const SampleArgs &a, int32_t b) {
+    constexpr int TPW = kWave / G, TPB = (NT / kWave) * TPW;
+    const int32_t g = a.gamma;
+    const int gl = threadIdx.x & (G - 1);
+    for (int32_t base = 0; base < g; base += TPB) {
+        const int32_t i = base + (int32_t)(threadIdx.x / G);
+        const bool has = i < g;
+        const int32_t t = has ? a.tokens[(size_t)b * g + i] : -1;
+        const bool valid = has && t >= 0 && t < a.Vt;
+        const void *trow = reinterpret_cast<const char *>(a.tl) +
+                           ((size_t)b * (g + 1) + (has ? i : 0)) * (size_t)a.Vt * Elem<DTT>::kBytes;
+        const void *drow = reinterpret_cast<const char *>(a.dl) +
+                           ((size_t)b * g + (has ? i : 0)) * (size_t)a.Vd * Elem<DTD>::kBytes;
+        Probe pr;
+        pr.zt = 0.0f;
+        pr.zd = -INFINITY;
+        if (valid && gl == 0) pr.zt = ld_logit<DTT>(trow, t);
+        if (a.d2t) {
+            const int32_t j = group_lower_bound<G>(a.d2t, a.Vd, valid ? t : 0);
+            if (valid && gl == 0 && j < a.Vd && a.d2t[j] == t) pr.zd = ld_logit<DTD>(drow, j);
+        } else if (valid && gl == 0) {
+            pr.zd = ld_logit<DTD>(drow, t);
+        }
+        if (has && gl == 0) pub(&a.probe[(size_t)b * g + i], pr);
+    }
+}
+
+template <int DTT, int DTD, int NT>
+__device__ __forceinline__ void probe_tokens(const SampleArgs &a, int32_t b) {
+    // the widest groups that still cover every token in one pass
+    constexpr int W = NT / kWave;
+    const int32_t g = a.gamma;
+    if (!a.d2t || g > 2 * W * 8) probe_tokens_g<DTT, DTD, NT, 8>(a, b);
+    else if (g <= W) probe_tokens_g<DTT, DTD, NT, 64>(a, b);
+    else if (g <= 2 * W) probe_tokens_g<DTT, DTD, NT, 32>(a, b);
+    else if (g <= 4 * W) probe_tokens_g<DTT, DTD, NT, 16>(a, b);
+    else probe_tokens_g<DTT, DTD, NT, 8>(a, b);
+}
+
+// Draft-id boundaries of the draw tiles under d2t: jb[k] = the first j with
+// d2t[j] >= k * tile, k = 0..ntiles.  Entry j (0 <= j <= Vd) owns the k with
+// d2t[j-1] < k * tile <= d2t[j] (d2t[-1] = -1, d2t[Vd] = +inf); the probe
+// workgroup of sequence b takes the j in [b (Vd+1) / B, (b+1) (Vd+1) / B).
+template <int NT>
+__device__ __forceinline__ void tile_bounds(const SampleArgs &a, int32_t b) {
+    const int64_t n1 = (int64_t)a.Vd + 1;
+    const int32_t j0 = (int32_t)(n1 * b / a.B), j1 = (int32_t)(n1 * (b + 1) / a.B);
+    for (int32_t j = j0 + (int32_t)threadIdx.x; j < j1; j += NT) {
+        const int64_t prev = j > 0 ? (int64_t)a.d2t[j - 1] : -1;
+        const int64_t cur = j < a.Vd ? (int64_t)a.d2t[j] : INT64_MAX;
+        const int64_t klo = prev < 0 ? 0 : prev / a.tile + 1;
+        int64_t khi = cur / a.tile;
+        if (khi > a.ntiles) khi = a.ntiles;
+        for (int64_t k = klo; k <= khi; ++k) a.tile_jb[k] = j;
+    }
+}
+
+// Grid: B probe workgroups, then B * ((gamma+1) * Ct + gamma * Cd) chunk
+// workgroups.  The last of a sequence's workgroups merges the chunk partials
+// of every row, runs the accept chain and records n for the draw.
 template <int DTT, int DTD, int NT, int U>
 __global__ __launch_bounds__(NT) void stats_kernel(SampleArgs a) {
+    static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
     __shared__ float s_m[NT / kWave], s_s[NT / kWave];
+    __shared__ MaxSum s_part[kPartCap];
     extern __shared__ RowDesc s_rows[];                       // [2 * gamma + 1]
     __shared__ int last_flag;
     __shared__ int32_t s_itmp[NT / kWave];
@@ -1299,101 +1505,565 @@ __global__ __launch_bounds__(NT) void stats_kernel(SampleArgs a) {
 
     const int32_t g = a.gamma, NR = 2 * g + 1;
     const int32_t per_seq = (g + 1) * a.Ct + g * a.Cd;
-    const int32_t b = blockIdx.x / per_seq, w = blockIdx.x % per_seq;
-    MaxSum *part = a.part + (size_t)b * per_seq;
-    MaxSum ms;
-    if (w < (g + 1) * a.Ct) {
-        const int32_t r = w / a.Ct, ch = w % a.Ct;
-        const void *row = reinterpret_cast<const char *>(a.tl) +
-                          ((size_t)b * (g + 1) + r) * (size_t)a.Vt * Elem<DTT>::kBytes;
-        ms = chunk_maxsum<DTT, NT, U>(row, a.Vt, ch, a.Ct, a.c, s_m, s_s);
+    int32_t b, w;
+    if ((int32_t)blockIdx.x < a.B) {
+        b = blockIdx.x;
+        w = -1;
     } else {
-        const int32_t w2 = w - (g + 1) * a.Ct;
-        const int32_t r = w2 / a.Cd, ch = w2 % a.Cd;
-        const void *row = reinterpret_cast<const char *>(a.dl) +
-                          ((size_t)b * g + r) * (size_t)a.Vd * Elem<DTD>::kBytes;
-        ms = chunk_maxsum<DTD, NT, U>(row, a.Vd, ch, a.Cd, a.c, s_m, s_s);
+        b = ((int32_t)blockIdx.x - a.B) / per_seq;
+        w = ((int32_t)blockIdx.x - a.B) % per_seq;
     }
-    if (threadIdx.x == 0) pub(&part[w], ms);
+    MaxSum *part = a.part + (size_t)b * per_seq;
+    if (w < 0) {
+        probe_tokens<DTT, DTD, NT>(a, b);
+        if (a.d2t) tile_bounds<NT>(a, b);
+    } else {
+        MaxSum ms;
+        if (w < (g + 1) * a.Ct) {
+            const int32_t r = w / a.Ct, ch = w % a.Ct;
+            const void *row = reinterpret_cast<const char *>(a.tl) +
+                              ((size_t)b * (g + 1) + r) * (size_t)a.Vt * Elem<DTT>::kBytes;
+            ms = chunk_maxsum<DTT, NT, U>(row, a.Vt, ch, a.Ct, a.c, s_m, s_s);
+        } else {
+            const int32_t w2 = w - (g + 1) * a.Ct;
+            const int32_t r = w2 / a.Cd, ch = w2 % a.Cd;
+            const void *row = reinterpret_cast<const char *>(a.dl) +
+                              ((size_t)b * g + r) * (size_t)a.Vd * Elem<DTD>::kBytes;
+            ms = chunk_maxsum<DTD, NT, U>(row, a.Vd, ch, a.Cd, a.c, s_m, s_s);
+        }
+        if (threadIdx.x == 0) pub(&part[w], ms);
+    }
 
-    if (!arrive_last(&a.cnt_stats[b], (uint32_t)per_seq, &last_flag)) return;
+    if (!arrive_last(&a.cnt_stats[b], (uint32_t)per_seq + 1u, &last_flag)) return;
 
+    // one round of loads: the chunk partials (into LDS), and this thread's
+    // draft position (token, probe, uniform)
     if (threadIdx.x == 0) s_status = 0;
+    const bool staged = per_seq <= kPartCap;
+    if (staged)
+        for (int32_t k = threadIdx.x; k < per_seq; k += NT) s_part[k] = sub(&part[k]);
+    const int32_t i = threadIdx.x;
+    int32_t t = -1;
+    Probe pr;
+    pr.zt = 0.0f;
+    pr.zd = -INFINITY;
+    double ua = 0.0;
+    if (i < g) {
+        t = a.tokens[(size_t)b * g + i];
+        pr = sub(&a.probe[(size_t)b * g + i]);
+        ua = (double)a.u_acc[(size_t)b * g + i];
+    }
     __syncthreads();
+    // row r is merged by thread r, chunk by chunk in order (identical rows
+    // give identical results)
     for (int32_t r = threadIdx.x; r < NR; r += NT) {
         const bool tgt = r <= g;
         const int32_t C = tgt ? a.Ct : a.Cd;
-        const MaxSum *p = tgt ? part + (size_t)r * a.Ct : part + (size_t)(g + 1) * a.Ct + (size_t)(r - g - 1) * a.Cd;
-        MaxSum t = sub(&p[0]);
-        for (int32_t k = 1; k < C; ++k) t = maxsum_merge(t, sub(&p[k]), a.c);
-        RowDesc d;
-        d.m = t.m;
-        d.Z = t.s;
-        d.Zk = t.s;
-        d.key = 0u;
-        d.tie_cut = INT32_MAX;
-        d.nkept = tgt ? a.Vt : a.Vd;
-        d.flags = bad_max(t.m) ? RD_NO_MASS : 0;
-        d.ptok = 0.0f;
-        if (d.flags & RD_NO_MASS) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
-        s_rows[r] = d;
-        a.rows[(size_t)b * NR + r] = d;
+        const int32_t off = tgt ? r * a.Ct : (g + 1) * a.Ct + (r - g - 1) * a.Cd;
+        MaxSum acc = staged ? s_part[off] : sub(&part[off]);
+        for (int32_t k = 1; k < C; ++k) acc = maxsum_merge(acc, staged ? s_part[off + k] : sub(&part[off + k]), a.c);
+        {
+            RowDesc d;
+            d.m = acc.m;
+            d.Z = acc.s;
+            d.Zk = acc.s;
+            d.key = 0u;
+            d.tie_cut = INT32_MAX;
+            d.nkept = tgt ? a.Vt : a.Vd;
+            d.flags = bad_max(acc.m) ? RD_NO_MASS : 0;
+            d.ptok = 0.0f;
+            if (d.flags & RD_NO_MASS) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
+            s_rows[r] = d;
+            a.rows[(size_t)b * NR + r] = d;
+        }
     }
     __syncthreads();
-    const int32_t n = accept_chain<DTT, DTD, NT>(a, b, s_rows, s_itmp, &s_status);
-    __syncthreads();
+    int32_t first_rej = INT32_MAX;
+    if (i < g) {
+        float pa = 0.0f, qc = 0.0f;
+        if (t < 0 || t >= a.Vt) {
+            atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
+        } else {
+            pa = row_prob(s_rows[i], pr.zt, t, a.c);
+            qc = row_prob(s_rows[g + 1 + i], pr.zd, t, a.c);
+        }
+        if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
+        if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
+        // u * q < p, exactly: both products fit a double
+        if (!(ua * (double)qc < (double)pa)) first_rej = i;
+    }
+    const int32_t fr = wg_min_i32<NT>(first_rej, s_itmp);
+    const int32_t n = fr == INT32_MAX ? g : fr;
+    if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? t : -1;
     if (threadIdx.x == 0) {
         SeqState st;
         st.n = n;
         st.status = s_status;
         st.pad0 = st.pad1 = 0;
+        st.dp = s_rows[n];
+        st.dq = s_rows[n < g ? g + 1 + n : n];
         a.seq[b] = st;
         a.out_len[b] = n;
         if (a.out_status) a.out_status[b] = s_status;
     }
 }
 
+// ---------------------------------------------------------------------------
+// Plain-mode draw.  Grid: B * ntiles; tile k covers target ids
+// [k * tile, (k+1) * tile), read with the row's 16-byte vectors (a vector that
+// straddles two tiles is read by both, each keeping its own ids).  Weights are
+// taken in fixed point, F(w) = floor(w * 2^52): tile masses and every prefix
+// are exact integers, so the pass that picks a tile and the pass that searches
+// inside it agree exactly whatever the order of the additions, and the draw
+// target floor(u * S) is exact.  Residual weights are F(max(0, p_t - q_t));
+// q_t comes from the draft row's vectors when it is laid out like the target
+// row, from a d2t scatter through LDS, or from single loads.  The last tile
+// workgroup of a sequence picks the tile and searches it.
+// ---------------------------------------------------------------------------
+
+// floor(w * 2^52) for 0 <= w < 2^11, from the bits of w (exact, no float64).
+__device__ __forceinline__ uint64_t fix52(float w) {
+    const uint32_t bits = __float_as_uint(w);
+    const int e = (int)((bits >> 23) & 0xffu);
+    const uint64_t m = (uint64_t)((bits & 0x7fffffu) | (e ? 0x800000u : 0u));
+    const int sh = (e ? e : 1) - 98;                 // w = m * 2^(e - 150), times 2^52
+    if (sh >= 0) return m << sh;
+    return sh > -24 ? m >> -sh : 0;
+}
+
+// One step of a wave reduction on a 64-bit value: add the value DPP-moved
+// under control CTRL (rows outside ROWMASK add 0).  No LDS traffic.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
+    return v + (((uint64_t)hi << 32) | lo);
+}
+// Sum over the 64 lanes, returned to every lane (all lanes must be active):
+// pairs, quads, half rows and rows by DPP permutes, then the rows are
+// chained through the row broadcasts so that lane 63 holds the total.
+__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v) {
+    v = dpp_add_u64<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v = dpp_add_u64<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v = dpp_add_u64<0x141, 0xf>(v);    // row_half_mirror
+    v = dpp_add_u64<0x140, 0xf>(v);    // row_mirror
+    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order (all lanes active):
+// shifts by 1, 2, 4, 8 inside each row of 16, then the row totals are carried
+// through the row broadcasts.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64_dpp(uint64_t v) {
+    v = dpp_add_u64<0x111, 0xf>(v);    // row_shr:1
+    v = dpp_add_u64<0x112, 0xf>(v);    // row_shr:2
+    v = dpp_add_u64<0x114, 0xf>(v);    // row_shr:4
+    v = dpp_add_u64<0x118, 0xf>(v);    // row_shr:8
+    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// floor(u * S) exactly, for a float32 u in [0, 1).
+__device__ __forceinline__ uint64_t frac_floor(float u, uint64_t S) {
+    const uint32_t bits = __float_as_uint(u);
+    const uint32_t e = (bits >> 23) & 0xffu;
+    const uint64_t m = e ? (uint64_t)((bits & 0x7fffffu) | 0x800000u) : (uint64_t)(bits & 0x7fffffu);
+    const int sh = e ? 150 - (int)e : 149;                   // u = m * 2^-sh
+    if (sh >= 128) return 0;
+    const unsigned __int128 pr = (unsigned __int128)m * S;
+    return (uint64_t)(pr >> sh);
+}
+
+// Exclusive prefix of one u64 per thread in thread order, and the total.
+template <int NT>
+__device__ __forceinline__ uint64_t wg_excl_scan_u64(uint64_t v, uint64_t *s_tmp, uint64_t *total) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const uint64_t inc = wave_incl_scan_u64(v);
+    if (lane == kWave - 1) s_tmp[w] = inc;
+    __syncthreads();
+    uint64_t base = 0, tot = 0;
+    for (int k = 0; k < NT / kWave; ++k) {
+        if (k < w) base += s_tmp[k];
+        tot += s_tmp[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + inc - v;
+}
+
+// One tile of a plain-mode draw, loaded: the vectors of target ids [t0, t1)
+// (U per thread, slice u = vectors v_lo + u * NT + tid), the draft values
+// where they come with the same vectors, and q of mapped ids in LDS.
 template <int DTT, int DTD, int NT>
-__global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
-    __shared__ float s_r[kTile];
-    __shared__ float s_q[kTile];
-    __shared__ float s_ftmp[NT / kWave];
-    __shared__ double s_dtmp[NT / kWave];
-    __shared__ int32_t s_itmp[NT / kWave];
-    __shared__ double s_bcast[4];
-    __shared__ int last_flag;
+struct DrawTile {
+    using ET = Elem<DTT>;
+    using ED = Elem<DTD>;
+    static constexpr int U = kTile / ET::kPerVec / NT + 1;
+    const void *trow, *drow;
+    RowSplit sp;
+    int32_t t0, t1, v_lo, v_hi;
+    float mp, izp, mq, izq, c;
+    bool resid, fused, mapped, nomass;
+    u32x4 rt[U], rd[U];
 
-    const int32_t g = a.gamma, NR = 2 * g + 1;
-    const int32_t b = blockIdx.x / a.ntiles, t = blockIdx.x % a.ntiles;
-    const SeqState st = a.seq[b];
-    const int32_t n = st.n;
-    DrawCtx x;
-    x.trow = reinterpret_cast<const char *>(a.tl) + ((size_t)b * (g + 1) + n) * (size_t)a.Vt * Elem<DTT>::kBytes;
-    x.drow = n < g ? reinterpret_cast<const char *>(a.dl) + ((size_t)b * g + n) * (size_t)a.Vd * Elem<DTD>::kBytes
+    // Weight of target id t (fixed point) given its target logit and q.
+    __device__ __forceinline__ uint64_t weight_q(float zt, float q) const {
+        const float p = nomass ? 0.0f : exp2_hw((zt - mp) * c) * izp;
+        if (!resid) return fix52(p);
+        return fix52(p - q > 0.0f ? p - q : 0.0f);
+    }
+    __device__ __forceinline__ float qprob(float zq) const { return exp2_hw((zq - mq) * c) * izq; }
+
+    // q of target id t when it does not come with the vectors
+    __device__ __forceinline__ float q_single(int32_t t, const float *s_q) const {
+        if (!resid) return 0.0f;
+        if (mapped) return s_q[t - t0];
+        return qprob(ED::load(drow, t));
+    }
+    // weights of the ids in slice u's vector of this thread, summed; f(t, w) per id
+    template <typename F>
+    __device__ __forceinline__ uint64_t slice(int u, const float *s_q, F &&f) const {
+        const int32_t v = v_lo + u * NT + (int32_t)threadIdx.x;
+        uint64_t s = 0;
+        if (v < v_hi) {
+            float zt[ET::kPerVec], zq[ET::kPerVec];
+            ET::unpack(rt[u], zt);
+            if constexpr (DTT == DTD) {
+                if (fused) ET::unpack(rd[u], zq);
+            }
+            const int32_t i0 = sp.head + v * ET::kPerVec;
+#pragma unroll
+            for (int k = 0; k < ET::kPerVec; ++k) {
+                const int32_t t = i0 + k;
+                if (t < t0 || t >= t1) continue;
+                float q = 0.0f;
+                if (resid) {
+                    if constexpr (DTT == DTD) q = fused ? qprob(zq[k]) : q_single(t, s_q);
+                    else q = q_single(t, s_q);
+                }
+                const uint64_t w = weight_q(zt[k], q);
+                f(t, w);
+                s += w;
+            }
+        }
+        return s;
+    }
+    // the ids of [t0, t1) outside the vector body (head or tail), one per
+    // thread: thread i takes the i-th of them
+    __device__ __forceinline__ int32_t edge_id() const {
+        const int32_t i = (int32_t)threadIdx.x;
+        const int32_t hb = max(t0, 0), he = min(t1, sp.head);          // head ids in the tile
+        const int32_t nh = he > hb ? he - hb : 0;
+        if (i < nh) return hb + i;
+        const int32_t tb = max(t0, sp.head + sp.nvec * ET::kPerVec), te = t1;
+        const int32_t ntl = te > tb ? te - tb : 0;
+        if (i - nh < ntl) return tb + (i - nh);
+        return -1;
+    }
+};
+
+template <int DTT, int DTD, int NT>
+__device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const SampleArgs &a, int32_t b,
+                                               int32_t n, const SeqState *st, int32_t k, int32_t j0, int32_t j1,
+                                               float *s_q) {
+    using ET = Elem<DTT>;
+    using ED = Elem<DTD>;
+    const int32_t g = a.gamma;
+    const RowDesc dp = load_desc(&st->dp), dq = load_desc(&st->dq);
+    x.trow = reinterpret_cast<const char *>(a.tl) + ((size_t)b * (g + 1) + n) * (size_t)a.Vt * ET::kBytes;
+    x.drow = n < g ? reinterpret_cast<const char *>(a.dl) + ((size_t)b * g + n) * (size_t)a.Vd * ED::kBytes
                    : nullptr;
-    x.d2t = a.d2t;
-    x.Vd = a.Vd;
-    x.dp = a.rows[(size_t)b * NR + n];
-    x.dq = n < g ? a.rows[(size_t)b * NR + g + 1 + n] : x.dp;
-    x.c = a.c;
     x.resid = n < g;
-    float *mass = a.tile_mass + (size_t)b * a.ntiles;
-    const float mt = tile_mass<DTT, DTD, NT>(x, t * kTile, min(a.Vt, (t + 1) * kTile), s_r, s_q, s_ftmp);
-    if (threadIdx.x == 0) pub_u32(&mass[t], __float_as_uint(mt));
-
-    if (!arrive_last(&a.cnt_draw[b], (uint32_t)a.ntiles, &last_flag)) return;
-
-    const double u = (double)a.u_s[b];
-    int32_t tok = draw_from_tiles<DTT, DTD, NT>(x, a.Vt, mass, a.ntiles, u, s_r, s_q, s_dtmp, s_itmp, s_bcast);
-    if (tok < 0 && x.resid) {
-        // zero residual mass (p == q on p's support): draw from p_n itself
-        x.resid = false;
-        for (int32_t k = 0; k < a.ntiles; ++k) {
-            const float m2 = tile_mass<DTT, DTD, NT>(x, k * kTile, min(a.Vt, (k + 1) * kTile), s_r, s_q, s_ftmp);
-            if (threadIdx.x == 0) pub_u32(&mass[k], __float_as_uint(m2));
+    x.mapped = x.resid && a.d2t != nullptr;
+    x.sp = row_split<DTT>(x.trow, a.Vt);
+    x.fused = false;
+    if constexpr (DTT == DTD)
+        if (x.resid && !x.mapped) x.fused = row_split<DTD>(x.drow, a.Vd).head == x.sp.head;
+    x.c = a.c;
+    x.mp = dp.m;
+    x.izp = 1.0f / dp.Zk;
+    x.nomass = (dp.flags & RD_NO_MASS) != 0;
+    x.mq = dq.m;
+    x.izq = (dq.flags & RD_NO_MASS) ? 0.0f : 1.0f / dq.Zk;
+    x.t0 = k * a.tile;
+    x.t1 = min(a.Vt, x.t0 + a.tile);
+    const int32_t body0 = x.sp.head, body1 = x.sp.head + x.sp.nvec * ET::kPerVec;
+    x.v_lo = x.t0 <= body0 ? 0 : (x.t0 - body0) / ET::kPerVec;
+    x.v_hi = x.t1 <= body0 ? 0 : min(x.sp.nvec, (min(x.t1, body1) - body0 + ET::kPerVec - 1) / ET::kPerVec);
+    const u32x4 *tb = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x.trow) +
+                                                      (size_t)x.sp.head * ET::kBytes);
+    // every load of the tile before any use (one round trip); indices are
+    // clamped into the tile's vectors and out-of-tile ids dropped when used
+    if (x.v_hi > x.v_lo) {
+#pragma unroll
+        for (int u = 0; u < DrawTile<DTT, DTD, NT>::U; ++u)
+            x.rt[u] = __builtin_nontemporal_load(&tb[min(x.v_lo + u * NT + (int32_t)threadIdx.x, x.v_hi - 1)]);
+        // keep these loads ahead of the draft-side loads below: the d2t
+        // scatter waits for those, and by then these must have arrived too
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DTT == DTD) {
+            if (x.fused) {
+                const u32x4 *db = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(x.drow) +
+                                                                  (size_t)x.sp.head * ED::kBytes);
+#pragma unroll
+                for (int u = 0; u < DrawTile<DTT, DTD, NT>::U; ++u)
+                    x.rd[u] = __builtin_nontemporal_load(&db[min(x.v_lo + u * NT + (int32_t)threadIdx.x, x.v_hi - 1)]);
+            }
+        }
+    }
+    if (x.mapped) {
+        // q of the mapped draft ids [j0, j1) (at most tile of them) into s_q
+        constexpr int UJ = kTile / NT;
+        int32_t tj[UJ];
+        float zq[UJ];
+        const bool any = j1 > j0;
+        if (any) {
+#pragma unroll
+            for (int u = 0; u < UJ; ++u) {
+                const int32_t j = min(j0 + u * NT + (int32_t)threadIdx.x, j1 - 1);
+                tj[u] = a.d2t[j];
+                zq[u] = ED::load(x.drow, j);
+            }
+        }
+        for (int32_t i = threadIdx.x; i < x.t1 - x.t0; i += NT) s_q[i] = 0.0f;
+        __syncthreads();
+        if (any) {
+#pragma unroll
+            for (int u = 0; u < UJ; ++u) {
+                const int32_t j = j0 + u * NT + (int32_t)threadIdx.x;
+                const int32_t i = tj[u] - x.t0;
+                if (j < j1 && i >= 0 && i < x.t1 - x.t0) s_q[i] = x.qprob(zq[u]);
+            }
         }
         __syncthreads();
-        tok = draw_from_tiles<DTT, DTD, NT>(x, a.Vt, mass, a.ntiles, u, s_r, s_q, s_dtmp, s_itmp, s_bcast);
+    }
+}
+
+template <int DTT, int DTD, int NT>
+__global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
+    using DT = DrawTile<DTT, DTD, NT>;
+    constexpr int U = DT::U;
+    constexpr int NW = NT / kWave;
+    __shared__ float s_q[kTile];
+    __shared__ uint64_t s_tmp[NW];
+    __shared__ uint64_t s_blk[(U + 2) * NW];      // search: per (slice, wave) totals, edge ids
+    __shared__ uint64_t s_pick[2];
+    __shared__ int32_t s_jr[2];
+    __shared__ int32_t s_tok;
+    __shared__ int last_flag;
+    // rare fallback (zero residual mass)
+    __shared__ double s_dtmp[NW];
+    __shared__ int32_t s_itmp[NW];
+    __shared__ int32_t s_j[2];
+
+    const int32_t g = a.gamma;
+    const int32_t b = blockIdx.x / a.ntiles, k = blockIdx.x % a.ntiles;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const SeqState *st = &a.seq[b];
+    const int32_t n = st->n;
+    int32_t j0 = 0, j1 = 0;
+    if (a.d2t) {
+        j0 = min(max(a.tile_jb[k], 0), a.Vd);
+        j1 = min(max(a.tile_jb[k + 1], j0), a.Vd);
+    }
+    DT x;
+    draw_tile_load<DTT, DTD, NT>(x, a, b, n, st, k, j0, j1, s_q);
+    uint64_t *mass = a.tile_mass + (size_t)b * a.ntiles;
+    {
+        auto none = [](int32_t, uint64_t) {};
+        uint64_t s = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) s += x.slice(u, s_q, none);
+        const int32_t te = x.edge_id();
+        if (te >= 0) s += x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q));
+        s = wave_total_u64(s);
+        if (lane == 0) s_tmp[wv] = s;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t m = 0;
+            for (int w = 0; w < NW; ++w) m += s_tmp[w];
+            pub_u64(&mass[k], m);
+        }
+    }
+
+    // two-level arrival: tiles of a sequence finish together, and one counter
+    // taking all of their atomics at once would serialize them
+    {
+        const int32_t ng = (a.ntiles + kDrawGroup - 1) / kDrawGroup;
+        uint32_t *cnt = a.cnt_draw + (size_t)b * (ng + 1);
+        const int32_t grp = k / kDrawGroup;
+        const uint32_t gsz = (uint32_t)min(kDrawGroup, a.ntiles - grp * kDrawGroup);
+        if (!arrive_last(&cnt[1 + grp], gsz, &last_flag)) return;
+        if (ng > 1 && !arrive_last(&cnt[0], (uint32_t)ng, &last_flag)) return;
+    }
+
+    const float u_s = a.u_s[b];
+    // S and the tile holding floor(u * S): one round of loads when the tiles
+    // fit one per thread (else a first sweep for S, a second for the pick)
+    uint64_t S = 0;
+    const int32_t rounds = (a.ntiles + NT - 1) / NT;
+    uint64_t mk0 = 0;
+    int32_t jr0 = 0, jr1 = 0;
+    for (int32_t r = 0; r < rounds; ++r) {
+        const int32_t kk = r * NT + (int32_t)threadIdx.x;
+        const uint64_t mk = kk < a.ntiles ? sub_u64(&mass[kk]) : 0;
+        if (r == 0) {
+            mk0 = mk;
+            if (a.d2t && kk < a.ntiles) {
+                jr0 = min(max(a.tile_jb[kk], 0), a.Vd);
+                jr1 = min(max(a.tile_jb[kk + 1], jr0), a.Vd);
+            }
+        }
+        const uint64_t t = wave_total_u64(mk);
+        if (lane == 0) s_tmp[wv] = t;
+        __syncthreads();
+        for (int w = 0; w < NW; ++w) S += s_tmp[w];
+        __syncthreads();
+    }
+    int32_t tok = -1;
+    if (S > 0) {
+        const uint64_t target = frac_floor(u_s, S);    // < S
+        if (threadIdx.x == 0) s_pick[0] = ~0ull;
+        uint64_t run = 0;
+        for (int32_t r = 0; r < rounds; ++r) {
+            const int32_t kk = r * NT + (int32_t)threadIdx.x;
+            const uint64_t mk = r == 0 ? mk0 : (kk < a.ntiles ? sub_u64(&mass[kk]) : 0);
+            const uint64_t inc = wave_incl_scan_u64_dpp(mk);
+            if (lane == kWave - 1) s_tmp[wv] = inc;
+            __syncthreads();
+            uint64_t base = run, tot = 0;
+            for (int w = 0; w < NW; ++w) {
+                if (w < wv) base += s_tmp[w];
+                tot += s_tmp[w];
+            }
+            const uint64_t ex = base + inc - mk;
+            if (kk < a.ntiles && mk > 0 && ex <= target && target < ex + mk) {
+                s_pick[0] = (uint64_t)kk;                 // the bracket is unique
+                s_pick[1] = target - ex;
+                if (a.d2t) {
+                    if (r > 0) {
+                        jr0 = min(max(a.tile_jb[kk], 0), a.Vd);
+                        jr1 = min(max(a.tile_jb[kk + 1], jr0), a.Vd);
+                    }
+                    s_jr[0] = jr0;
+                    s_jr[1] = jr1;
+                }
+            }
+            run += tot;
+            __syncthreads();
+        }
+        if (s_pick[0] < (uint64_t)a.ntiles) {
+            const int32_t kp = (int32_t)s_pick[0];
+            const uint64_t tin = s_pick[1];
+            const int32_t pj0 = a.d2t ? s_jr[0] : 0, pj1 = a.d2t ? s_jr[1] : 0;
+            __syncthreads();
+            draw_tile_load<DTT, DTD, NT>(x, a, b, n, st, kp, pj0, pj1, s_q);
+            // order of the tile's ids: the head ids, the slices (thread order
+            // inside each), the tail ids.  Each wave puts its slice totals in
+            // LDS; every thread then finds the block holding tin by itself.
+            auto none = [](int32_t, uint64_t) {};
+            uint64_t su[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) su[u] = x.slice(u, s_q, none);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t t = wave_total_u64(su[u]);
+                if (lane == 0) s_blk[u * NW + wv] = t;
+            }
+            // head / tail ids (at most 7 of each) exist in the first and last tiles only
+            const int32_t body1 = x.sp.head + x.sp.nvec * Elem<DTT>::kPerVec;
+            const bool edges = x.t0 < x.sp.head || x.t1 > body1;
+            if (threadIdx.x < 2) s_blk[U * NW + threadIdx.x] = 0;
+            if (threadIdx.x == 0) s_tok = -1;
+            if (edges) {
+                __syncthreads();
+                const int32_t te = x.edge_id();
+                if (te >= 0)
+                    atomicAdd(reinterpret_cast<unsigned long long *>(&s_blk[U * NW + (te < x.sp.head ? 0 : 1)]),
+                              (unsigned long long)x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q)));
+            }
+            __syncthreads();
+            // blocks in id order: head, (u, w) for u, w ascending, tail
+            int blk = -3;                               // the tail unless found earlier
+            uint64_t off;
+            {
+                uint64_t r = s_blk[U * NW];
+                if (tin < r) {
+                    blk = -2;
+                    off = tin;
+                } else {
+                    off = tin - r;
+                    for (int i = 0; i < U * NW; ++i) {
+                        const uint64_t m = s_blk[i];
+                        if (blk == -3 && m > 0 && tin < r + m) {
+                            blk = i;
+                            off = tin - r;
+                        }
+                        r += m;
+                    }
+                    if (blk == -3) off = tin - r;
+                }
+            }
+            if (blk >= 0) {
+                // wave blk % NW, slice blk / NW: the lane whose prefix brackets off
+                const int bu = blk / NW, bw = blk % NW;
+                if (wv == bw) {
+                    uint64_t mine = 0;
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (u == bu) mine = su[u];
+                    const uint64_t inc = wave_incl_scan_u64_dpp(mine);
+                    const uint64_t exc = inc - mine;
+                    if (mine > 0 && exc <= off && off < inc) {
+                        uint64_t rr = exc;
+                        int32_t found = -1;
+                        auto walk = [&](int32_t t, uint64_t w) {
+                            if (found < 0 && w > 0) {
+                                rr += w;
+                                if (rr > off) found = t;
+                            }
+                        };
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            if (u == bu) (void)x.slice(u, s_q, walk);
+                        s_tok = found;
+                    }
+                }
+            } else if (threadIdx.x == 0) {
+                // head (blk == -2) or tail (blk == -3) ids, walked in order
+                const int32_t lo = blk == -2 ? max(x.t0, 0) : max(x.t0, body1);
+                const int32_t hi = blk == -2 ? min(x.t1, x.sp.head) : x.t1;
+                uint64_t rr = 0;
+                int32_t found = -1, lastpos = -1;
+                for (int32_t t = lo; t < hi && found < 0; ++t) {
+                    const uint64_t w = x.weight_q(Elem<DTT>::load(x.trow, t), x.q_single(t, s_q));
+                    if (w > 0) {
+                        lastpos = t;
+                        rr += w;
+                        if (rr > off) found = t;
+                    }
+                }
+                s_tok = found >= 0 ? found : lastpos;
+            }
+            __syncthreads();
+            tok = s_tok;
+        }
+    } else if (n < g) {
+        // zero residual mass (p == q wherever p > 0): draw from p_n itself
+        DrawCtx y;
+        y.trow = x.trow;
+        y.drow = x.drow;
+        y.d2t = nullptr;
+        y.Vd = a.Vd;
+        y.dp = load_desc(&st->dp);
+        y.dq = y.dp;
+        y.c = a.c;
+        y.resid = false;
+        tok = draw_row_one_wg<DTT, DTD, NT>(y, a.Vt, a.tile, (double)u_s, s_q, s_dtmp, s_itmp, s_j);
     }
     if (threadIdx.x == 0) a.out_tokens[(size_t)b * (g + 1) + n] = tok;
 }
@@ -1401,34 +2071,56 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
 // ---------------------------------------------------------------------------
 // Host side: workspace layout and launches
 // ---------------------------------------------------------------------------
-int32_t stats_chunks(int32_t V, int /*dtype*/) {
-    // elements per workgroup, counted as bfloat16 vectors so that the chunk
-    // count depends on V only (a float32 chunk is twice the bytes)
-    const int64_t per = (int64_t)kStatsThreads * kStatsUnroll * kStatsItersPerWg * 8;
+
+// Chunks per row in plain mode: about 64 KiB of logits each, cut further
+// (down to kStatsMinChunk elements) while the grid has fewer than
+// kStatsMinWgs workgroups.  A function of the row length, element size and row
+// count only, so rows of equal length and type are cut the same way
+// (identical rows give identical statistics).
+static int32_t plain_chunks(int32_t V, int32_t ebytes, int64_t rows) {
+    const int64_t per = (int64_t)kStatsChunkBytes / ebytes;
     int64_t C = ((int64_t)V + per - 1) / per;
+    const int64_t want = (kStatsMinWgs + rows - 1) / (rows > 0 ? rows : 1);
+    int64_t cap = (int64_t)V / kStatsMinChunk;
+    if (cap < 1) cap = 1;
+    const int64_t extra = want < cap ? want : cap;
+    if (extra > C) C = extra;
     if (C < 1) C = 1;
     if (C > kMaxChunks) C = kMaxChunks;
     return (int32_t)C;
 }
 
-bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int dt_t, int dt_d, bool topp,
-                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *ntiles) {
-    const int32_t ct = topp ? 1 : stats_chunks(Vt, dt_t);
-    const int32_t cd = topp ? 1 : stats_chunks(Vd, dt_d);
-    const int32_t nt = (Vt + kTile - 1) / kTile;
+// Target ids per draw tile: kTile, halved (down to kTileMin) until the draw
+// has kDrawMinWgs workgroups.
+static int32_t draw_tile(int32_t B, int32_t Vt) {
+    int32_t tl = kTile;
+    while (tl > kTileMin && (int64_t)B * ((Vt + tl - 1) / tl) < kDrawMinWgs) tl >>= 1;
+    return tl;
+}
+
+bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt, int32_t bd, bool topp,
+                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *tile, int32_t *ntiles) {
     const size_t NR = (size_t)(2 * gamma + 1);
+    const int32_t ct = topp ? 1 : plain_chunks(Vt, bt, (int64_t)B * (int64_t)NR);
+    const int32_t cd = topp ? 1 : plain_chunks(Vd, bd, (int64_t)B * (int64_t)NR);
+    const int32_t tl = draw_tile(B, Vt);
+    const int32_t nt = (Vt + tl - 1) / tl;
     L->cnt_stats = 0;
     L->cnt_draw = align256(sizeof(uint32_t) * (size_t)B);
-    L->counter_bytes = 2 * align256(sizeof(uint32_t) * (size_t)B);
+    L->counter_bytes = L->cnt_draw +
+                       align256(sizeof(uint32_t) * (size_t)B * (size_t)(1 + (nt + kDrawGroup - 1) / kDrawGroup));
     size_t off = 0;
     L->seq = off;       off = align256(off + sizeof(SeqState) * (size_t)B);
     L->rows = off;      off = align256(off + sizeof(RowDesc) * (size_t)B * NR);
-    L->part = off;      off = align256(off + sizeof(MaxSum) * (size_t)B * ((size_t)(gamma + 1) * ct + (size_t)gamma * cd));
+    L->part = off;      off = align256(off + (topp ? 0 : sizeof(MaxSum) * (size_t)B * ((size_t)(gamma + 1) * ct + (size_t)gamma * cd)));
     L->kept = off;      off = align256(off + (topp ? sizeof(KeptEnt) * (size_t)B * NR * kKeptCap : 0));
-    L->tile_mass = off; off = align256(off + sizeof(float) * (size_t)B * nt);
+    L->probe = off;     off = align256(off + (topp ? 0 : sizeof(Probe) * (size_t)B * (size_t)gamma));
+    L->tile_mass = off; off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt));
+    L->tile_jb = off;   off = align256(off + (topp ? 0 : sizeof(int32_t) * ((size_t)nt + 1)));
     L->data_bytes = off;
     *Ct = ct;
     *Cd = cd;
+    *tile = tl;
     *ntiles = nt;
     return true;
 }
@@ -1442,7 +2134,7 @@ static hipError_t launch_sample_dt(const SampleArgs &a, hipStream_t st) {
         return hipGetLastError();
     }
     const int64_t per_seq = (int64_t)(a.gamma + 1) * a.Ct + (int64_t)a.gamma * a.Cd;
-    hipLaunchKernelGGL((stats_kernel<DTT, DTD, kStatsThreads, kStatsUnroll>), dim3((unsigned)(a.B * per_seq)),
+    hipLaunchKernelGGL((stats_kernel<DTT, DTD, kStatsThreads, kStatsUnroll>), dim3((unsigned)(a.B * (1 + per_seq))),
                        dim3(kStatsThreads), sizeof(RowDesc) * (size_t)NR, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
