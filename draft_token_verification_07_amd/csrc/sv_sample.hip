@@ -40,11 +40,12 @@ namespace sv {
 // compact in the instruction cache; inlined otherwise.
 #ifdef SV_RARE_OUTLINE
 #define SV_RARE __attribute__((noinline))
-#define SV_TOPP_OCCUPANCY __attribute__((amdgpu_waves_per_eu(6)))
 #else
 #define SV_RARE __forceinline__
-#define SV_TOPP_OCCUPANCY
 #endif
+// Three 512-thread top-p workgroups per CU (24 waves, so at most 80 VGPRs)
+// keep every row of a 64 x 11-row batch resident at once.
+#define SV_TOPP_OCCUPANCY __attribute__((amdgpu_waves_per_eu(6)))
 
 // ---------------------------------------------------------------------------
 // Row descriptors
@@ -323,50 +324,27 @@ __device__ __forceinline__ void tile_jrange(const DrawCtx &x, int32_t t0, int32_
 template <int DTT, int DTD, int NT>
 __device__ __forceinline__ void tile_fill(const DrawCtx &x, int32_t t0, int32_t len, int32_t j0, int32_t j1,
                                           float *s_w) {
-    constexpr int U = kTile / NT;
+    // These whole-row draws are rare paths: plain loops that keep few
+    // registers live (the kernels they sit in are sized for their hot paths).
     const bool scat = x.resid && x.d2t != nullptr && j1 > j0;
     const bool dense_q = x.resid && x.d2t == nullptr;
-    // Loads are unconditional, at clamped indices (a load under a divergent
-    // branch is waited for inside it, one round trip each); out-of-range
-    // values are masked afterwards.  The branches below are uniform.
-    float z[U], zq[U];
-    int32_t jt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) z[u] = ld_logit<DTT>(x.trow, t0 + min(u * NT + (int32_t)threadIdx.x, len - 1));
-    if (dense_q) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) zq[u] = ld_logit<DTD>(x.drow, t0 + min(u * NT + (int32_t)threadIdx.x, len - 1));
-    } else if (scat) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t j = min(j0 + u * NT + (int32_t)threadIdx.x, j1 - 1);
-            jt[u] = x.d2t[j];
-            zq[u] = ld_logit<DTD>(x.drow, j);
-        }
-    }
     if (scat) {
         for (int32_t k = threadIdx.x; k < len; k += NT) s_w[k] = 0.0f;
         __syncthreads();
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t j = j0 + u * NT + (int32_t)threadIdx.x;
-            const int32_t k = jt[u] - t0;
-            if (j < j1 && (uint32_t)k < (uint32_t)len) s_w[k] = row_prob(x.dq, zq[u], j, x.c);
+        for (int32_t j = j0 + (int32_t)threadIdx.x; j < j1; j += NT) {
+            const int32_t k = x.d2t[j] - t0;
+            if ((uint32_t)k < (uint32_t)len) s_w[k] = row_prob(x.dq, ld_logit<DTD>(x.drow, j), j, x.c);
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int32_t k = u * NT + (int32_t)threadIdx.x;
-        if (k < len) {
-            float r = row_prob(x.dp, z[u], t0 + k, x.c);
-            if (x.resid) {
-                // q: scattered from the mapped draft ids, or the same id's draft logit
-                const float q = scat ? s_w[k] : dense_q ? row_prob(x.dq, zq[u], t0 + k, x.c) : 0.0f;
-                r = r - q > 0.0f ? r - q : 0.0f;
-            }
-            s_w[k] = r;
+    for (int32_t k = threadIdx.x; k < len; k += NT) {
+        float r = row_prob(x.dp, ld_logit<DTT>(x.trow, t0 + k), t0 + k, x.c);
+        if (x.resid) {
+            // q: scattered from the mapped draft ids, or the same id's draft logit
+            const float q = scat ? s_w[k] : dense_q ? row_prob(x.dq, ld_logit<DTD>(x.drow, t0 + k), t0 + k, x.c) : 0.0f;
+            r = r - q > 0.0f ? r - q : 0.0f;
         }
+        s_w[k] = r;
     }
     __syncthreads();
 }
@@ -644,6 +622,30 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
 // Wave-aggregated LDS append: every lane of the wave calls it; lanes with
 // pred get consecutive slots from *counter, with one atomic per wave instead
 // of one per lane (same-address LDS atomics serialise lane by lane).
+// Inclusive prefix sum of one int per lane over the wave, by DPP row shifts
+// and row broadcasts (all lanes active).
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return v;
+}
+// Reserve n slots per lane in a shared list with one LDS atomic per wave;
+// returns this lane's first slot.  All lanes call it together.
+__device__ __forceinline__ int32_t wave_append_n(int32_t n, int32_t *counter) {
+    const int32_t inc = wave_incl_scan_i32(n);
+    const int32_t tot = __builtin_amdgcn_readlane(inc, kWave - 1);
+    int32_t base = 0;
+    if (tot > 0) {
+        if ((threadIdx.x & (kWave - 1)) == 0) base = atomicAdd(counter, tot);
+        base = __builtin_amdgcn_readlane(base, 0);
+    }
+    return base + inc - n;
+}
+
 __device__ __forceinline__ int32_t wave_append(bool pred, int32_t *counter) {
     const uint64_t bal = __ballot(pred);
     if (bal == 0) return -1;
@@ -863,22 +865,29 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
                 }
             }
     };
+    // A partial iteration (the first or the last): the loads are issued
+    // unconditionally at clamped indices (a load under a divergent branch is
+    // waited for inside it, one round trip per vector); vectors past the row
+    // are masked afterwards.  Requires sp.nvec >= 1.
     auto load_iter = [&](int32_t it, u32x4 (&raw)[U], float (&xv)[U][E::kPerVec], float (&vm)[U],
                          float &tm) -> int {
         const int32_t vbase = it * U * NT + threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[min(vbase + u * NT, sp.nvec - 1)]);
         int nu = 0;
         tm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const bool ok = vbase + u * NT < sp.nvec;
+            E::unpack(raw[u], xv[u]);
             vm[u] = -INFINITY;
-            if (vbase + u * NT < sp.nvec) {
-                raw[u] = __builtin_nontemporal_load(&body[vbase + u * NT]);
-                E::unpack(raw[u], xv[u]);
 #pragma unroll
-                for (int k = 0; k < E::kPerVec; ++k) vm[u] = fmaxf(vm[u], xv[u][k]);
-                tm = fmaxf(tm, vm[u]);
-                nu = u + 1;
+            for (int k = 0; k < E::kPerVec; ++k) {
+                if (!ok) xv[u][k] = -INFINITY;
+                vm[u] = fmaxf(vm[u], xv[u][k]);
             }
+            tm = fmaxf(tm, vm[u]);
+            nu += ok ? 1 : 0;
         }
         return nu;
     };
@@ -895,7 +904,20 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         __syncthreads();
         tile(raw, xv, vm, tm, threadIdx.x, nu);
     }
+    int prio = -1;
     for (int32_t it = 1; it < full; ++it) {
+        {
+            // waves with more of their row left issue first, so that rows
+            // sharing a CU finish together instead of oldest-first
+            const int lvl = (int)(((int64_t)(full - it) * 4) / (full + 1));
+            if (lvl != prio) {
+                prio = lvl;
+                if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+                else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+                else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
+        }
         const int32_t vbase = it * U * NT + threadIdx.x;
         u32x4 raw[U];
 #pragma unroll
@@ -962,6 +984,8 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
             const int32_t pos = wave_append(in, &s_ncand);
             if (in && pos < kCandCap) s_cand[pos] = ((uint64_t)zkey(z) << 32) | (uint32_t)j;
         };
+        // one vector per thread: its in-band elements take consecutive slots
+        // (one LDS atomic per wave)
         for (int32_t t0 = 0; t0 < nvc; t0 += NT) {
             const int32_t t = t0 + (int32_t)threadIdx.x;
             const bool valid = t < nvc;
@@ -974,12 +998,23 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
 #pragma unroll
                 for (int k = 0; k < E::kPerVec; ++k) x[k] = -INFINITY;
             }
+            uint32_t mask = 0;
 #pragma unroll
-            for (int k = 0; k < E::kPerVec; ++k) put(valid, x[k], i0 + k);
+            for (int k = 0; k < E::kPerVec; ++k)
+                if (x[k] >= thr_final && x[k] > -INFINITY) mask |= 1u << k;
+            int32_t pos = wave_append_n((int32_t)__popc(mask), &s_ncand);
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k)
+                if ((mask >> k) & 1u) {
+                    if (pos < kCandCap) s_cand[pos] = ((uint64_t)zkey(x[k]) << 32) | (uint32_t)(i0 + k);
+                    ++pos;
+                }
         }
-        {
+        if (sp.head > 0) {
             const bool vh = threadIdx.x < (unsigned)sp.head;
             put(vh, vh ? E::load(row, threadIdx.x) : -INFINITY, threadIdx.x);
+        }
+        if (sp.tail > 0) {
             const int32_t jt = sp.head + sp.nvec * E::kPerVec + threadIdx.x;
             const bool vt = threadIdx.x < (unsigned)sp.tail;
             put(vt, vt ? E::load(row, jt) : -INFINITY, jt);
@@ -1048,6 +1083,7 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
                         const int32_t i = t % n2, sl = t / n2;
                         const int32_t j0 = (int32_t)((int64_t)n2 * sl / S), j1 = (int32_t)((int64_t)n2 * (sl + 1) / S);
                         const uint64_t Pi = s_P[i];
+#pragma unroll 8
                         for (int32_t j = j0; j < j1; ++j)
                             acc += s_P[j] > Pi ? ((1ull << 48) | (uint64_t)s_fw[j]) : 0ull;
                         if (S > 1) atomicAdd(reinterpret_cast<unsigned long long *>(&s_ahead[i]), (unsigned long long)acc);
@@ -1142,27 +1178,48 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
 template <int DTT, int DTD, int NT>
 __device__ __forceinline__ int32_t draw_from_list(const SampleArgs &a, int32_t b, int32_t n, const RowDesc &dp,
                                                   const RowDesc &dq, const KeptEnt *list, const KeptEnt *qlist,
+                                                  const KeptEnt *pre_list, const KeptEnt *pre_qlist,
                                                   uint64_t *s_lds, double u, double *s_dtmp, int32_t *s_itmp) {
+    // pre_list / pre_qlist: copies of the lists already in LDS, or null
     const int32_t g = a.gamma;
     const int32_t K = dp.nkept;
     const bool resid = n < g;
     const void *drow = resid ? reinterpret_cast<const char *>(a.dl) +
                                    ((size_t)b * g + n) * (size_t)a.Vd * Elem<DTD>::kBytes
                              : nullptr;
-    // q's kept list in LDS as (target id, q) pairs
+    // q's kept list in LDS as an open-addressing hash table from target id
+    // to q (at most half full), so each p entry finds its q in a probe or two
     const int32_t Kq = (resid && (dq.flags & RD_HAS_LIST) && dq.nkept <= kQListCap) ? dq.nkept : -1;
-    int32_t *s_qid = reinterpret_cast<int32_t *>(s_lds);                     // [kQListCap]
-    float *s_qv = reinterpret_cast<float *>(s_lds) + kQListCap;              // [kQListCap]
-    uint64_t *s_work = s_lds + kQListCap;                                    // past the q list
+    constexpr int kHash = 2 * kQListCap;
+    int32_t *s_hid = reinterpret_cast<int32_t *>(s_lds);                     // [kHash], -1 = empty
+    float *s_hq = reinterpret_cast<float *>(s_lds) + kHash;                  // [kHash]
+    uint64_t *s_work = s_lds + kHash;                                        // past the table
+    auto hslot = [](int32_t id) { return (int32_t)(((uint32_t)id * 0x9E3779B1u) >> 21) & (kHash - 1); };
     // one round trip for both lists: this thread's p entry and q entries
     KeptEnt e;
     e.id = INT32_MAX;
     e.w = 0.0f;
-    if (K <= NT && (int32_t)threadIdx.x < K) e = sub(&list[threadIdx.x]);
-    for (int32_t j = threadIdx.x; j < Kq; j += NT) {
-        const KeptEnt qe = sub(&qlist[j]);
-        s_qid[j] = a.d2t ? a.d2t[qe.id] : qe.id;
-        s_qv[j] = qe.w / dq.Zk;
+    if (K <= NT && (int32_t)threadIdx.x < K) e = pre_list ? pre_list[threadIdx.x] : sub(&list[threadIdx.x]);
+    constexpr int kQPer = (kQListCap + NT - 1) / NT;
+    KeptEnt qe[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int32_t j = (int32_t)threadIdx.x + k * NT;
+        if (j < Kq) qe[k] = pre_qlist ? pre_qlist[j] : sub(&qlist[j]);
+    }
+    if (Kq >= 0) {
+        for (int32_t i = threadIdx.x; i < kHash; i += NT) s_hid[i] = -1;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kQPer; ++k) {
+            const int32_t j = (int32_t)threadIdx.x + k * NT;
+            if (j < Kq) {
+                const int32_t id = a.d2t ? a.d2t[qe[k].id] : qe[k].id;
+                int32_t sl = hslot(id);
+                while (atomicCAS(&s_hid[sl], -1, id) != -1) sl = (sl + 1) & (kHash - 1);
+                s_hq[sl] = qe[k].w / dq.Zk;
+            }
+        }
     }
     __syncthreads();
     auto weight = [&](const KeptEnt &pe, bool use_resid) -> float {
@@ -1170,8 +1227,15 @@ __device__ __forceinline__ int32_t draw_from_list(const SampleArgs &a, int32_t b
         if (use_resid) {
             float q = 0.0f;
             if (Kq >= 0) {
-                for (int32_t j = 0; j < Kq; ++j)
-                    if (s_qid[j] == pe.id) q = s_qv[j];
+                // ids within a list are distinct; the table is never full
+                for (int32_t sl = hslot(pe.id);; sl = (sl + 1) & (kHash - 1)) {
+                    const int32_t h = s_hid[sl];
+                    if (h == pe.id) {
+                        q = s_hq[sl];
+                        break;
+                    }
+                    if (h == -1) break;
+                }
             } else if (a.d2t) {
                 const int32_t j = lower_bound_i32(a.d2t, a.Vd, pe.id);
                 if (j < a.Vd && a.d2t[j] == pe.id) q = row_prob(dq, ld_logit<DTD>(drow, j), j, a.c);
@@ -1197,6 +1261,7 @@ __device__ __forceinline__ int32_t draw_from_list(const SampleArgs &a, int32_t b
             if (threadIdx.x == 0) *s_tok = -1;
             __syncthreads();
             uint64_t incl = 0, S = 0;
+#pragma unroll 8
             for (int32_t j = 0; j < K; ++j) {
                 const uint64_t r = s_rf[j];
                 S += r;
@@ -1263,6 +1328,12 @@ __device__ SV_RARE int32_t draw_full_row(const SampleArgs &a, int32_t b, int32_t
     return tok;
 }
 
+// Kept-list prefixes staged by the sequence epilogue, at the end of the
+// band area (past what the draws use).
+constexpr int kPreBase = 4096;                 // u64 offset in the band area
+constexpr int kPreSlots = 1536;                // list entries (8 bytes each)
+constexpr int kPreMax = 64;                    // entries per row at most
+
 // With the rare paths out of line, three 512-thread workgroups per CU (24
 // waves, <= 80 VGPRs) keep every row of a 64 x 11-row batch resident.
 template <int DTT, int DTD, int NT, int U>
@@ -1276,6 +1347,10 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     static_assert(sizeof(RowDesc) * (2 * SV_MAX_GAMMA + 1) <= sizeof(uint64_t) * 4096,
                   "row descriptors must fit the band area");
     static_assert(sizeof(uint64_t) * kKeptCap <= sizeof(uint64_t) * 4096, "list sort must fit the band area");
+    static_assert(2 * kQListCap + kKeptCap <= kPreBase, "q table and list sort stay below the list prefixes");
+    static_assert(2 * kQListCap + NT / 2 + NT + 1 <= kPreBase, "q table and pairwise draw stay below the prefixes");
+    static_assert(kPreBase + kPreSlots <= 2 * kCandCap + kCandCap / 2 + 512, "list prefixes fit the band area");
+    static_assert(kPreSlots / (2 * SV_MAX_GAMMA + 1) >= 1, "every row gets a prefix slot");
     static_assert(kTile * sizeof(float) <= sizeof(uint64_t) * 4096, "draw tiles must fit the band area");
     __shared__ int last_flag;
     __shared__ int32_t s_itmp[NT / kWave];
@@ -1311,8 +1386,20 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     if (!arrive_last(&a.cnt_stats[b], (uint32_t)NR, &last_flag)) return;
 
     // ---- sequence epilogue: accept chain, then the draw ----
+    // one round of loads: the row descriptors, this thread's draft position
+    // (token, uniform) and the sampling uniform
     RowDesc *s_rows = reinterpret_cast<RowDesc *>(s_cand);   // the row work is done
+    const int32_t *x = a.tokens + (size_t)b * g;
+    const int32_t ti = (int32_t)threadIdx.x < g ? x[threadIdx.x] : 0;
+    const double ui = (int32_t)threadIdx.x < g ? (double)a.u_acc[(size_t)b * g + threadIdx.x] : 0.0;
+    const double u = (double)a.u_s[b];
     for (int32_t k = threadIdx.x; k < NR; k += NT) s_rows[k] = sub(&rows[k]);
+    // the first kPre entries of every row's kept list, loaded in the same
+    // round (entries past a row's own count are stale and never used)
+    KeptEnt *s_pre = reinterpret_cast<KeptEnt *>(s_cand + kPreBase);
+    const int32_t kPre = min(kPreMax, kPreSlots / NR);
+    for (int32_t e = threadIdx.x; e < NR * kPre; e += NT)
+        s_pre[e] = sub(&a.kept[((size_t)b * NR + e / kPre) * kKeptCap + e % kPre]);
     if (threadIdx.x == 0) s_status = 0;
     __syncthreads();
     for (int32_t k = threadIdx.x; k < NR; k += NT)
@@ -1320,30 +1407,29 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     int32_t n;
     {
         // every row has published the probability of its own draft token
-        const int32_t *x = a.tokens + (size_t)b * g;
+        static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
+        const int32_t i = threadIdx.x;
         int32_t first_rej = INT32_MAX;
-        for (int32_t i = threadIdx.x; i < g; i += NT) {
-            const int32_t t = x[i];
-            if (t < 0 || t >= a.Vt) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
+        if (i < g) {
+            if (ti < 0 || ti >= a.Vt) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
             const float pa = s_rows[i].ptok, qc = s_rows[g + 1 + i].ptok;
             if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
             if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
-            const double uu = (double)a.u_acc[(size_t)b * g + i];
-            if (!(uu * (double)qc < (double)pa) && i < first_rej) first_rej = i;
+            if (!(ui * (double)qc < (double)pa)) first_rej = i;
         }
         const int32_t fr = wg_min_i32<NT>(first_rej, s_itmp);
         n = fr == INT32_MAX ? g : fr;
-        for (int32_t i = threadIdx.x; i <= g; i += NT)
-            if (i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? x[i] : -1;
+        if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? ti : -1;
     }
     const RowDesc dp = s_rows[n];
     const RowDesc dq = n < g ? s_rows[g + 1 + n] : dp;
-    const double u = (double)a.u_s[b];
     __syncthreads();                                          // s_rows is reused below
     int32_t tok;
     if (dp.flags & RD_HAS_LIST) {
+        const KeptEnt *pl = dp.nkept <= kPre ? s_pre + (size_t)n * kPre : nullptr;
+        const KeptEnt *pq = (n < g && dq.nkept <= kPre) ? s_pre + (size_t)(g + 1 + n) * kPre : nullptr;
         tok = draw_from_list<DTT, DTD, NT>(a, b, n, dp, dq, a.kept + ((size_t)b * NR + n) * kKeptCap,
-                                           a.kept + ((size_t)b * NR + g + 1 + n) * kKeptCap, s_cand, u,
+                                           a.kept + ((size_t)b * NR + g + 1 + n) * kKeptCap, pl, pq, s_cand, u,
                                            s_dtmp, s_itmp);
     } else {
         // kept set too large for a list: tile-by-tile over the whole row
