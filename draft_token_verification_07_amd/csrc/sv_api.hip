@@ -19,13 +19,22 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 // The whole grid must fit one launch dimension.
 bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
 
-// greedy / tree: counters [B] below K, (value, index) partials [B, R, C] above
-size_t greedy_counter_bytes(int32_t B) { return align256(sizeof(uint32_t) * (size_t)B); }
+// greedy / tree: counters [B] (+ [B, R] when rows are chunked) below K;
+// (value, index) row results [B, R] and chunk partials [B, R, C] above
+int32_t greedy_C(int32_t B, int32_t R, int32_t V) { return greedy_chunks(V, (int64_t)B * R); }
+size_t greedy_group_offset(int32_t B, int32_t R, int32_t V) {
+    return (size_t)B * (greedy_C(B, R, V) > 1 ? 1 + (size_t)R : 1);
+}
+size_t greedy_counter_bytes(int32_t B, int32_t R, int32_t V) {
+    const size_t ng = (size_t)(R + kRowGroup - 1) / kRowGroup;
+    return align256(sizeof(uint32_t) * (greedy_group_offset(B, R, V) + (ng > 1 ? (size_t)B * ng : 0)));
+}
+size_t greedy_rowres_bytes(int32_t B, int32_t R) { return align256(sizeof(ArgMax) * (size_t)B * R); }
 size_t greedy_data_bytes(int32_t B, int32_t R, int32_t V) {
-    return align256(sizeof(int32_t) * 2 * (size_t)B * R * greedy_chunks(V, SV_BF16));
+    return greedy_rowres_bytes(B, R) + align256(sizeof(ArgMax) * (size_t)B * R * greedy_C(B, R, V));
 }
 size_t greedy_ws(int32_t B, int32_t R, int32_t V) {
-    return workspace_need(greedy_counter_bytes(B), greedy_data_bytes(B, R, V));
+    return workspace_need(greedy_counter_bytes(B, R, V), greedy_data_bytes(B, R, V));
 }
 
 sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, const int32_t *parents,
@@ -38,17 +47,20 @@ sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, con
     a.B = B;
     a.rows_per_seq = R;
     a.V = V;
-    a.chunks = greedy_chunks(V, dt);
+    a.chunks = greedy_C(B, R, V);
     a.tree = tree ? 1 : 0;
     a.out_tokens = out_tokens;
     a.out_len = out_len;
     a.out_status = out_status;
     a.out_path = out_path;
-    if (!workspace_fits(ws_bytes, greedy_counter_bytes(B), greedy_data_bytes(B, R, V)))
+    if (!workspace_fits(ws_bytes, greedy_counter_bytes(B, R, V), greedy_data_bytes(B, R, V)))
         return SV_ERR_WORKSPACE_TOO_SMALL;
     char *base = static_cast<char *>(ws);
+    char *data = base + counter_region(ws_bytes);
     a.counters = reinterpret_cast<uint32_t *>(base);
-    a.part = reinterpret_cast<ArgMax *>(base + counter_region(ws_bytes));
+    a.group_counters = (int64_t)greedy_group_offset(B, R, V);
+    a.rowres = reinterpret_cast<ArgMax *>(data);
+    a.part = reinterpret_cast<ArgMax *>(data + greedy_rowres_bytes(B, R));
     if (!grid_fits((int64_t)B * R * a.chunks)) return SV_ERR_TOO_LARGE;
     return launch_greedy(a, dt, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

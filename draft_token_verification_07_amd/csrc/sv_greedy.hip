@@ -25,8 +25,8 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     __shared__ ArgMax red[NT / kWave];
     __shared__ int last_flag;
     __shared__ int32_t s_n, s_status;
-    // epilogue scratch, sized by the launch: gmax[R] int32, then (tree) tok[R],
-    // par[R] int32, depth[R] int16, acc[R] uint8
+    // epilogue scratch, sized by the launch: gmax[R], tok[R] int32, then
+    // (tree) par[R] int32, depth[R] int16, acc[R] uint8
     extern __shared__ int32_t gmax[];
 
     const int32_t R = a.rows_per_seq, C = a.chunks;
@@ -57,13 +57,23 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     const u32x4 *body = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(rowp) +
                                                         (size_t)s.head * E::kBytes);
     int32_t v = lo + tid;
-    for (; v + (U - 1) * NT < hi; v += U * NT) {
+    // U vectors per lane per round, all loaded before any is used.  Loads
+    // are unconditional: in the last round they are clamped to the chunk's
+    // last vector and the repeats are masked to -inf (a load under a
+    // divergent branch would be waited for inside it, one round trip each).
+    for (; v < hi; v += U * NT) {
         u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[v + u * NT]);
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[min(v + u * NT, hi - 1)]);
         float x[U][E::kPerVec];
 #pragma unroll
-        for (int u = 0; u < U; ++u) E::unpack(raw[u], x[u]);
+        for (int u = 0; u < U; ++u) {
+            E::unpack(raw[u], x[u]);
+            if (v + u * NT >= hi) {
+#pragma unroll
+                for (int k = 0; k < E::kPerVec; ++k) x[u][k] = -INFINITY;
+            }
+        }
         float tm = x[0][0];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -80,12 +90,6 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
             best.i = idx;
         }
     }
-    for (; v < hi; v += NT) {
-        float x[E::kPerVec];
-        E::unpack(__builtin_nontemporal_load(&body[v]), x);
-#pragma unroll
-        for (int k = 0; k < E::kPerVec; ++k) one(x[k], s.head + v * E::kPerVec + k);
-    }
     if (c == C - 1 && tid < s.tail) {
         const int32_t i = s.head + s.nvec * E::kPerVec + tid;
         one(E::load(rowp, i), i);
@@ -93,43 +97,72 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     best = wave_argmax(best);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = best;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        ArgMax r0 = red[0];
-        for (int w = 1; w < NT / kWave; ++w) r0 = argmax_merge(r0, red[w]);
-        pub(&a.part[(size_t)row * C + c], r0);
+    ArgMax r0 = red[0];
+    for (int w = 1; w < NT / kWave; ++w) r0 = argmax_merge(r0, red[w]);
+
+    // ---- rows cut in several chunks: the last chunk of a row merges them ---
+    // (two arrival levels, so that no counter takes every chunk of a
+    // sequence at once)
+    if (C > 1) {
+        if (threadIdx.x == 0) pub(&a.part[(size_t)row * C + c], r0);
+        if (!arrive_last(&a.counters[a.B + row], (uint32_t)C, &last_flag)) return;
+        __shared__ ArgMax s_ch[kMaxChunksMerged];
+        for (int32_t k = threadIdx.x; k < C; k += NT) {
+            const ArgMax m = sub(&a.part[(size_t)row * C + k]);
+            if (k < kMaxChunksMerged) s_ch[k] = m;
+        }
+        __syncthreads();
+        r0 = s_ch[0];
+        for (int32_t k = 1; k < C; ++k)                                  // chunk order
+            r0 = argmax_merge(r0, k < kMaxChunksMerged ? s_ch[k] : sub(&a.part[(size_t)row * C + k]));
     }
+    if (threadIdx.x == 0) pub(&a.rowres[row], r0);
 
     // ---- last workgroup of the sequence: combine and walk ----------------
-    if (!arrive_last(&a.counters[b], (uint32_t)(R * C), &last_flag)) return;
+    // Rows of a sequence finish together; with many rows, a first arrival
+    // level per group of kRowGroup rows keeps the atomics on one counter few.
+    {
+        const int32_t ng = (R + kRowGroup - 1) / kRowGroup;
+        if (ng > 1) {
+            const int32_t grp = (row % R) / kRowGroup;
+            const uint32_t gsz = (uint32_t)min(kRowGroup, R - grp * kRowGroup);
+            if (!arrive_last(&a.counters[a.group_counters + (size_t)b * ng + grp], gsz, &last_flag)) return;
+            if (!arrive_last(&a.counters[b], (uint32_t)ng, &last_flag)) return;
+        } else if (!arrive_last(&a.counters[b], (uint32_t)R, &last_flag)) {
+            return;
+        }
+    }
 
-    if (threadIdx.x == 0) { s_status = 0; s_n = 0; }
-    __syncthreads();
+    // one round of loads: the row results, the draft tokens (and parents)
+    static_assert(NT >= kWave, "one wave at least");
+    const int32_t nt = a.tree ? R : R - 1;               // tokens per sequence
+    if (threadIdx.x == 0) { s_status = 0; s_n = a.tree ? 0 : R - 1; }
+    int32_t *tok = gmax + R;                              // [R] (tree and chain)
+    int32_t *par = tok + R;                               // [R] (tree)
     for (int32_t r = threadIdx.x; r < R; r += NT) {
-        const ArgMax *p = a.part + ((size_t)b * R + r) * C;
-        ArgMax m = sub(&p[0]);
-        for (int32_t k = 1; k < C; ++k) m = argmax_merge(m, sub(&p[k]));
+        const ArgMax m = sub(&a.rowres[(size_t)b * R + r]);
+        const int32_t t = r < nt ? a.tokens[(size_t)b * nt + r] : 0;
+        const int32_t p = a.tree ? a.parents[(size_t)b * R + r] : 0;
         // a row of -inf everywhere: the lowest id attaining the maximum is 0
-        if (m.i == INT32_MAX) m.i = 0;
+        gmax[r] = m.i == INT32_MAX ? 0 : m.i;
+        tok[r] = t;
+        if (a.tree) par[r] = p;
         if (!(m.v > -INFINITY) || m.v == INFINITY) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
-        gmax[r] = m.i;
+        const bool tok_used = a.tree ? r >= 1 : r < nt;
+        if (tok_used && (t < 0 || t >= a.V)) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
+        if (a.tree && r >= 1 && (p < 0 || p >= r)) atomicOr(&s_status, (int)SV_SEQ_BAD_PARENT);
     }
     __syncthreads();
 
     if (!a.tree) {
         // chain: x_i are the draft tokens, i < gamma = R - 1
         const int32_t g = R - 1;
-        const int32_t *x = a.tokens + (size_t)b * g;
-        if (threadIdx.x == 0) s_n = g;
-        __syncthreads();
-        for (int32_t i = threadIdx.x; i < g; i += NT) {
-            const int32_t xi = x[i];
-            if (xi < 0 || xi >= a.V) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
-            if (xi != gmax[i]) atomicMin(&s_n, i);        // first mismatch
-        }
+        for (int32_t i = threadIdx.x; i < g; i += NT)
+            if (tok[i] != gmax[i]) atomicMin(&s_n, i);        // first mismatch
         __syncthreads();
         const int32_t n = s_n;
         for (int32_t i = threadIdx.x; i <= g; i += NT)
-            a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? x[i] : (i == n ? gmax[n] : -1);
+            a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? tok[i] : (i == n ? gmax[n] : -1);
         if (threadIdx.x == 0) {
             a.out_len[b] = n;
             if (a.out_status) a.out_status[b] = s_status;
@@ -137,23 +170,41 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
         return;
     }
 
-    // tree: node k >= 1 has parent par[k] < k and token tok[k]
+    // tree: node k >= 1 has parent par[k] < k and token tok[k].  Node k is
+    // accepted iff every edge on its path to the root matches (the edge into
+    // k matches when tok[k] is the argmax of the parent's row); a node with
+    // a bad parent is accepted by no one below it.
     const int32_t N = R;
-    // tokens and parents are staged in LDS so the serial walk below never
-    // waits on global memory
-    int32_t *tok = gmax + N;
-    int32_t *par = tok + N;
     int16_t *depth = reinterpret_cast<int16_t *>(par + N);
-    uint8_t *acc = reinterpret_cast<uint8_t *>(depth + N);
-    for (int32_t k = threadIdx.x; k < N; k += NT) {
-        tok[k] = a.tokens[(size_t)b * N + k];
-        par[k] = a.parents[(size_t)b * N + k];
-        if (k >= 1 && (tok[k] < 0 || tok[k] >= a.V)) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
-        if (k >= 1 && (par[k] < 0 || par[k] >= k)) atomicOr(&s_status, (int)SV_SEQ_BAD_PARENT);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
+    if (N <= kWave) {
+        // one wave, pointer jumping: after round r every node points 2^r
+        // levels up (or at its root) and carries the AND of the edges and the
+        // length of the path jumped so far
+        if (threadIdx.x < kWave) {
+            const int32_t k = threadIdx.x;
+            const bool node = k < N;
+            const int32_t p = node ? par[k] : 0;
+            const bool root = k == 0 || !node || p < 0 || p >= k;
+            int32_t up = root ? k : p;
+            bool ok = root ? (k == 0) : tok[k] == gmax[p];
+            int32_t dep = root ? 0 : 1;
+            for (int r = 0; r < 6; ++r) {                  // 2^6 = 64 >= any depth here
+                const int32_t up2 = __shfl(up, up, kWave);
+                const bool ok2 = __shfl((int)ok, up, kWave) != 0;
+                const int32_t dep2 = __shfl(dep, up, kWave);
+                ok = ok && ok2;
+                dep += dep2;
+                up = up2;
+            }
+            // the deepest accepted node, lowest index on ties
+            const int32_t key = (node && ok) ? (dep << 16) | (0xffff - k) : -1;
+            const int32_t best = wave_max(key);
+            if (node) depth[k] = (int16_t)dep;
+            if (k == 0) s_n = best >= 0 ? 0xffff - (best & 0xffff) : 0;
+        }
+    } else if (threadIdx.x == 0) {
         // parents precede children, so one pass in index order settles every node
+        uint8_t *acc = reinterpret_cast<uint8_t *>(depth + N);
         acc[0] = 1;
         depth[0] = 0;
         int32_t best_k = 0;
@@ -190,18 +241,26 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
 template <int DT>
 static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st) {
     const size_t R = (size_t)a.rows_per_seq;
-    const size_t lds = R * sizeof(int32_t) + (a.tree ? R * (2 * sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
+    // gmax[R], tok[R], then (tree) par[R], depth[R] int16, acc[R] uint8
+    const size_t lds = 2 * R * sizeof(int32_t) + (a.tree ? R * (sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
     hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll>), dim3(grid),
                        dim3(kGreedyThreads), lds, st, a);
     return hipGetLastError();
 }
 
 // Chunks per row.  Counted in 8-element vectors whatever the dtype, so the
-// workspace size depends on V only (a float32 chunk is twice the bytes).
-int32_t greedy_chunks(int32_t V, int /*dtype*/) {
+// workspace size depends on V and the row count only (a float32 chunk is
+// twice the bytes).  Rows are cut further, down to kGreedyMinChunkVecs
+// vectors, while the grid has fewer than kGreedyMinWgs workgroups.
+int32_t greedy_chunks(int32_t V, int64_t rows) {
     const int64_t nvec = ((int64_t)V + 7) / 8;
     const int64_t target = (int64_t)kGreedyThreads * kGreedyUnroll * kGreedyItersPerWg;
     int64_t C = (nvec + target - 1) / target;
+    const int64_t want = (kGreedyMinWgs + rows - 1) / (rows > 0 ? rows : 1);
+    int64_t cap = nvec / kGreedyMinChunkVecs;
+    if (cap < 1) cap = 1;
+    const int64_t extra = want < cap ? want : cap;
+    if (extra > C) C = extra;
     if (C < 1) C = 1;
     if (C > kMaxChunks) C = kMaxChunks;
     return (int32_t)C;

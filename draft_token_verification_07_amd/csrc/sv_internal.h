@@ -25,6 +25,9 @@ struct MaxSum;
 #ifndef SV_GREEDY_ITERS
 #define SV_GREEDY_ITERS 16
 #endif
+#ifndef SV_GREEDY_MIN_WGS
+#define SV_GREEDY_MIN_WGS 256
+#endif
 #ifndef SV_STATS_THREADS
 #define SV_STATS_THREADS 256
 #endif
@@ -44,6 +47,10 @@ struct MaxSum;
 constexpr int kGreedyThreads = SV_GREEDY_THREADS;
 constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
 constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
+constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
+constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
+constexpr int kMaxChunksMerged = 256;               // chunk results a row merge stages in LDS
+constexpr int kRowGroup = 8;                        // rows per first-level arrival counter
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
 constexpr int kStatsUnroll = SV_STATS_UNROLL;
 constexpr int kStatsItersPerWg = SV_STATS_ITERS;
@@ -88,11 +95,14 @@ struct GreedyArgs {
     int32_t B, rows_per_seq, V, chunks;
     int32_t tree;
     int32_t *out_tokens, *out_len, *out_status, *out_path;
-    ArgMax *part;              // [B * rows_per_seq * chunks]
-    uint32_t *counters;        // [B]
+    ArgMax *part;              // [B * rows_per_seq * chunks] chunk results (chunks > 1)
+    ArgMax *rowres;            // [B * rows_per_seq] row results
+    uint32_t *counters;        // [B] sequences, [B * rows_per_seq] rows (chunks > 1),
+                               // then from group_counters [B * ceil(rows_per_seq / kRowGroup)]
+    int64_t group_counters;    // offset of the row-group counters in counters
 };
 
-int32_t greedy_chunks(int32_t V, int dtype);
+int32_t greedy_chunks(int32_t V, int64_t rows);
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t st);
 
 // ---------------------------------------------------------------------------
