@@ -101,6 +101,25 @@ def test_tree_bad_parent_and_chain(oracle_mod):
     assert g["status"][0] & 8 and g["status"][1] & 8 and g["status"][2] & 1
 
 
+@pytest.mark.parametrize("B,N,V,depth,chain", [(3, 64, 4099, 63, True), (2, 65, 2053, 64, True),
+                                               (3, 64, 8191, 63, False), (2, 200, 1031, 12, False)])
+def test_tree_deep_and_large(oracle_mod, B, N, V, depth, chain):
+    # trees up to 64 nodes are walked by one wave (pointer jumping, depth up
+    # to 63); larger ones by the serial walk.  Every token matches (p_match 1)
+    # so that the deepest paths are accepted.
+    w = synth.tree(300 + N, B=B, N=N, V=V, max_depth=depth, max_children=8, p_match=1.0)
+    if chain:
+        w["parents"][0] = np.arange(-1, N - 1, dtype=np.int32)
+        am = np.argmax(synth.bf16_to_f32(w["target"][0]), axis=-1)
+        w["tokens"][0, 1:] = am[w["parents"][0, 1:]]
+    _say("tree deep", B, N, V, depth, chain)
+    g = run_tree(w)
+    o = oracle_mod.verify_tree_greedy(w["target"], w["tokens"], w["parents"])
+    assert_same(g, o, ["path", "tokens", "accept_len", "status"])
+    if chain:
+        assert g["accept_len"][0] == N - 1
+
+
 def test_tree_full_size(oracle_mod):
     w = synth.tree(5005)              # B=16, N=32, V=49152 bf16
     _say("tree full")
