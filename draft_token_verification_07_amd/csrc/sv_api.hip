@@ -194,6 +194,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.rows = reinterpret_cast<RowDesc *>(data + L.rows);
     a.part = reinterpret_cast<MaxSum *>(data + L.part);
     a.kept = reinterpret_cast<KeptEnt *>(data + L.kept);
+    a.kept_stride = kept_stride(Vt, Vd);
     a.probe = reinterpret_cast<Probe *>(data + L.probe);
     a.tile_mass = reinterpret_cast<uint64_t *>(data + L.tile_mass);
     a.tile_jb = reinterpret_cast<int32_t *>(data + L.tile_jb);

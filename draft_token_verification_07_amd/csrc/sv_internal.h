@@ -163,7 +163,8 @@ struct SampleArgs {
     SeqState *seq;             // [B]
     RowDesc *rows;             // [B, 2*gamma+1]: target rows then draft rows
     MaxSum *part;              // [B, (gamma+1)*Ct + gamma*Cd]
-    KeptEnt *kept;             // [B, 2*gamma+1, kKeptCap] (top-p only)
+    KeptEnt *kept;             // [B, 2*gamma+1, kept_stride] (top-p only)
+    int32_t kept_stride;       // min(kKeptCap, max(Vt, Vd))
     Probe *probe;              // [B, gamma] (plain mode)
     uint64_t *tile_mass;       // [B, ntiles] fixed-point draw masses (plain mode)
     int32_t *tile_jb;          // [ntiles + 1] first draft id of each draw tile under d2t (plain mode)
@@ -196,6 +197,7 @@ struct WorkspaceLayout {
 // largest layout, which the workspace size query assumes.
 bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt, int32_t bd, bool topp,
                    WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *tile, int32_t *ntiles);
+int32_t kept_stride(int32_t Vt, int32_t Vd);
 hipError_t launch_sample(const SampleArgs &a, int dt_t, int dt_d, hipStream_t st);
 
 }  // namespace sv

@@ -1362,7 +1362,7 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     const int32_t b = blockIdx.x / NR, r = blockIdx.x % NR;
     const float band = kToppBandNats * a.T;
     RowDesc *rows = a.rows + (size_t)b * NR;
-    KeptEnt *kept = a.kept + ((size_t)b * NR + r) * kKeptCap;
+    KeptEnt *kept = a.kept + ((size_t)b * NR + r) * a.kept_stride;
     {
         // row r: target rows 0..g, then draft rows; each carries the draft
         // token it scores (none for the bonus row)
@@ -1399,7 +1399,7 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     KeptEnt *s_pre = reinterpret_cast<KeptEnt *>(s_cand + kPreBase);
     const int32_t kPre = min(kPreMax, kPreSlots / NR);
     for (int32_t e = threadIdx.x; e < NR * kPre; e += NT)
-        s_pre[e] = sub(&a.kept[((size_t)b * NR + e / kPre) * kKeptCap + e % kPre]);
+        s_pre[e] = sub(&a.kept[((size_t)b * NR + e / kPre) * a.kept_stride + min(e % kPre, a.kept_stride - 1)]);
     if (threadIdx.x == 0) s_status = 0;
     __syncthreads();
     for (int32_t k = threadIdx.x; k < NR; k += NT)
@@ -1428,8 +1428,8 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     if (dp.flags & RD_HAS_LIST) {
         const KeptEnt *pl = dp.nkept <= kPre ? s_pre + (size_t)n * kPre : nullptr;
         const KeptEnt *pq = (n < g && dq.nkept <= kPre) ? s_pre + (size_t)(g + 1 + n) * kPre : nullptr;
-        tok = draw_from_list<DTT, DTD, NT>(a, b, n, dp, dq, a.kept + ((size_t)b * NR + n) * kKeptCap,
-                                           a.kept + ((size_t)b * NR + g + 1 + n) * kKeptCap, pl, pq, s_cand, u,
+        tok = draw_from_list<DTT, DTD, NT>(a, b, n, dp, dq, a.kept + ((size_t)b * NR + n) * a.kept_stride,
+                                           a.kept + ((size_t)b * NR + g + 1 + n) * a.kept_stride, pl, pq, s_cand, u,
                                            s_dtmp, s_itmp);
     } else {
         // kept set too large for a list: tile-by-tile over the whole row
@@ -2184,6 +2184,12 @@ static int32_t draw_tile(int32_t B, int32_t Vt) {
     return tl;
 }
 
+// Kept-list slots per row: a row keeps at most as many ids as it has.
+int32_t kept_stride(int32_t Vt, int32_t Vd) {
+    const int32_t v = Vt > Vd ? Vt : Vd;
+    return v < kKeptCap ? v : kKeptCap;
+}
+
 bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt, int32_t bd, bool topp,
                    WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *tile, int32_t *ntiles) {
     const size_t NR = (size_t)(2 * gamma + 1);
@@ -2199,7 +2205,7 @@ bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt,
     L->seq = off;       off = align256(off + sizeof(SeqState) * (size_t)B);
     L->rows = off;      off = align256(off + sizeof(RowDesc) * (size_t)B * NR);
     L->part = off;      off = align256(off + (topp ? 0 : sizeof(MaxSum) * (size_t)B * ((size_t)(gamma + 1) * ct + (size_t)gamma * cd)));
-    L->kept = off;      off = align256(off + (topp ? sizeof(KeptEnt) * (size_t)B * NR * kKeptCap : 0));
+    L->kept = off;      off = align256(off + (topp ? sizeof(KeptEnt) * (size_t)B * NR * kept_stride(Vt, Vd) : 0));
     L->probe = off;     off = align256(off + (topp ? 0 : sizeof(Probe) * (size_t)B * (size_t)gamma));
     L->tile_mass = off; off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt));
     L->tile_jb = off;   off = align256(off + (topp ? 0 : sizeof(int32_t) * ((size_t)nt + 1)));
