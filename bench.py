@@ -274,7 +274,11 @@ def main():
     ms_per_step = total_ms / K
     rows = rows_per_step(w)
     value = rows * K / (total_ms / 1e3)
-    achieved = nbytes / (mean_launch_ms / 1e3) / 1e9
+    # Average launch duration: the throughput lap's events bracket K launches
+    # that run back to back on the launch stream, so total / K is the mean
+    # launch-to-launch duration (for the two-kernel paths, of the call).  The
+    # per-launch lap, with events between launches, is reported beside it.
+    achieved = nbytes / (ms_per_step / 1e3) / 1e9
     traffic = read_traffic(args.traffic_table, args.workload)
 
     cpu = None
