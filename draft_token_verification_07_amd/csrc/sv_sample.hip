@@ -608,6 +608,76 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
     return v;
 }
 
+// One step of a wave reduction on a 64-bit value: add the value DPP-moved
+// under control CTRL (rows outside ROWMASK add 0).  No LDS traffic.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
+    return v + (((uint64_t)hi << 32) | lo);
+}
+// Sum over the 64 lanes, returned to every lane (all lanes must be active):
+// pairs, quads, half rows and rows by DPP permutes, then the rows are
+// chained through the row broadcasts so that lane 63 holds the total.
+__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v) {
+    v = dpp_add_u64<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v = dpp_add_u64<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v = dpp_add_u64<0x141, 0xf>(v);    // row_half_mirror
+    v = dpp_add_u64<0x140, 0xf>(v);    // row_mirror
+    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order (all lanes active):
+// shifts by 1, 2, 4, 8 inside each row of 16, then the row totals are carried
+// through the row broadcasts.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64_dpp(uint64_t v) {
+    v = dpp_add_u64<0x111, 0xf>(v);    // row_shr:1
+    v = dpp_add_u64<0x112, 0xf>(v);    // row_shr:2
+    v = dpp_add_u64<0x114, 0xf>(v);    // row_shr:4
+    v = dpp_add_u64<0x118, 0xf>(v);    // row_shr:8
+    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
+// The same reduction pattern on floats: maximum, then sum, over the wave.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_max_f32(float v) {
+    const float w = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROWMASK, 0xf, false));
+    return fmaxf(v, w);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_add_f32(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, false));
+}
+// Online-softmax partials (m, s) of the 64 lanes combined, returned to every
+// lane: the wave maximum M first, then the sum of s * 2^((m - M) * c).
+__device__ __forceinline__ MaxSum wave_maxsum_dpp(MaxSum a, float c) {
+    float m = a.m;
+    m = dpp_max_f32<0xB1, 0xf>(m);
+    m = dpp_max_f32<0x4E, 0xf>(m);
+    m = dpp_max_f32<0x141, 0xf>(m);
+    m = dpp_max_f32<0x140, 0xf>(m);
+    m = dpp_max_f32<0x142, 0xa>(m);
+    m = dpp_max_f32<0x143, 0xc>(m);
+    MaxSum r;
+    r.m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+    float s = a.m > -INFINITY ? a.s * exp2_hw((a.m - r.m) * c) : 0.0f;
+    s = dpp_add_f32<0xB1, 0xf>(s);
+    s = dpp_add_f32<0x4E, 0xf>(s);
+    s = dpp_add_f32<0x141, 0xf>(s);
+    s = dpp_add_f32<0x140, 0xf>(s);
+    s = dpp_add_f32<0x142, 0xa>(s);
+    s = dpp_add_f32<0x143, 0xc>(s);
+    r.s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 63));
+    return r;
+}
+
 // Inclusive prefix sum of a u64 across a wave (lane order).
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -803,6 +873,183 @@ __device__ SV_RARE void band_radix(const uint64_t *s_P, const uint32_t *s_fw, un
 // copied to LDS), then expand the band, select the kept set, and publish the
 // row descriptor and kept list.  s_lds is 32 KiB: band tokens in its first
 // half, band vectors in its second.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Top-p select over the band by bins (the usual case).  The band tokens are
+// binned by their distance below the row maximum: kWave bins of equal width,
+// so a lower bin holds only larger logits and equal logits share a bin.  Per-bin
+// fixed-point mass and count give, by a scan that every wave runs alike, the
+// bin holding the boundary; only that bin's tokens are ranked against each
+// other.  The kept set is every band token whose ordering code is at least
+// the boundary's -- the set the general path finds.  Four workgroup barriers.
+// Returns false, having written nothing to global memory and left the band
+// vectors in LDS, when the row needs the general path.
+constexpr int kBinMembers = 224;        // tokens of the boundary bin ranked here
+
+struct BinSelectLds {
+    uint64_t *P;          // [kCandCap] ordering codes of the band tokens
+    uint32_t *fw;         // [kCandCap] their fixed-point weights
+    uint64_t *bm;         // [kWave] bin masses (zero on entry)
+    uint32_t *bc;         // [kWave] bin counts (zero on entry)
+    uint64_t *mP;         // [kBinMembers] the boundary bin's tokens
+    uint32_t *mfw;        // [kBinMembers]
+    int32_t *cnt;         // [3] tokens, boundary-bin tokens, kept entries (zero on entry)
+    uint64_t *res;        // [3] boundary code (zero on entry), kept mass, kept count
+    float *ptok;          // zero on entry
+};
+
+template <int DT, int NT>
+__device__ __forceinline__ bool bin_select(const void *row, const RowSplit &sp, int32_t L, int32_t nvc,
+                                           const u32x4 *s_cvec, const int32_t *s_cvid, const BinSelectLds &l,
+                                           float m, float Z, float c, float band, float top_p, int32_t xtok,
+                                           const int32_t *d2t, RowDesc *out, KeptEnt *kept) {
+    using E = Elem<DT>;
+    constexpr int NB = kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const double T0 = (double)top_p * (double)Z;
+    if (!(T0 < kFixSelMaxMass)) return false;
+    const uint64_t T0f = (uint64_t)(T0 * kFixW);
+    const float thr = m - band;
+    const float bscale = (float)NB / band;
+    auto bin_of = [&](float z) { return (int)fminf((m - z) * bscale, (float)(NB - 1)); };
+    // -0 is folded onto +0 so that the ordering code orders values
+    auto put = [&](int32_t pos, float z, int32_t id) {
+        if (pos < kCandCap) {
+            const float zf = z + 0.0f;
+            const uint32_t fw = fixw32(zf, m, c);
+            l.P[pos] = pcode(fkey(zf), id);
+            l.fw[pos] = fw;
+            const int bn = bin_of(zf);
+            atomicAdd(reinterpret_cast<unsigned long long *>(&l.bm[bn]), (unsigned long long)fw);
+            atomicAdd(&l.bc[bn], 1u);
+        }
+    };
+
+    // A. band tokens: one band vector per thread, its tokens in consecutive slots
+    for (int32_t t0 = 0; t0 < nvc; t0 += NT) {
+        const int32_t t = t0 + (int32_t)threadIdx.x;
+        float x[E::kPerVec];
+        int32_t i0 = 0;
+        if (t < nvc) {
+            E::unpack(s_cvec[t], x);
+            i0 = sp.head + s_cvid[t] * E::kPerVec;
+        } else {
+#pragma unroll
+            for (int k = 0; k < E::kPerVec; ++k) x[k] = -INFINITY;
+        }
+        uint32_t mask = 0;
+#pragma unroll
+        for (int k = 0; k < E::kPerVec; ++k)
+            if (x[k] >= thr && x[k] > -INFINITY) mask |= 1u << k;
+        int32_t pos = wave_append_n((int32_t)__popc(mask), &l.cnt[0]);
+#pragma unroll
+        for (int k = 0; k < E::kPerVec; ++k)
+            if ((mask >> k) & 1u) put(pos++, x[k], i0 + k);
+    }
+    if (sp.head + sp.tail > 0) {
+        // elements outside the vector body (rows not 16-byte aligned)
+        const int32_t i = threadIdx.x;
+        const bool v = i < sp.head + sp.tail;
+        const int32_t j = i < sp.head ? i : sp.head + sp.nvec * E::kPerVec + (i - sp.head);
+        const float z = v ? E::load(row, j) : -INFINITY;
+        const bool in = v && z >= thr && z > -INFINITY;
+        const int32_t pos = wave_append(in, &l.cnt[0]);
+        if (in) put(pos, z, j);
+    }
+    __syncthreads();
+
+    // B. the boundary bin, in every wave alike: the first bin whose inclusive
+    // mass exceeds T0 (the band must hold more than T0, with the margin of the
+    // general path); then its tokens, compacted
+    const int32_t n = l.cnt[0];
+    if (n > kCandCap) return false;
+    const uint64_t bm = l.bm[lane];
+    const int32_t bc = (int32_t)l.bc[lane];
+    const uint64_t binc = wave_incl_scan_u64_dpp(bm);
+    const int32_t cinc = wave_incl_scan_i32(bc);
+    const uint64_t total = readlane_u64(binc, kWave - 1);
+    if (!((double)total > (double)T0f * (1.0 + 1e-5))) return false;
+    const int bstar = __ffsll((unsigned long long)__ballot(binc > T0f)) - 1;
+    const uint64_t before = readlane_u64(binc - bm, bstar);
+    const int32_t cbefore = __builtin_amdgcn_readlane(cinc - bc, bstar);
+    const int32_t nmem = __builtin_amdgcn_readlane(bc, bstar);
+    if (nmem > kBinMembers) return false;
+    for (int32_t t0 = 0; t0 < n; t0 += NT) {
+        const int32_t t = t0 + (int32_t)threadIdx.x;
+        uint64_t P = 0;
+        bool in = false;
+        if (t < n) {
+            P = l.P[t];
+            in = bin_of(fkey_inv(pkey(P))) == bstar;
+        }
+        const int32_t pos = wave_append(in, &l.cnt[1]);
+        if (in && pos < kBinMembers) {
+            l.mP[pos] = P;
+            l.mfw[pos] = l.fw[t];
+        }
+    }
+    __syncthreads();
+
+    // C. the boundary token: the mass strictly ahead of it <= T0 < that plus
+    // its own weight (exactly one token of the bin)
+    const int32_t nm = l.cnt[1];
+    if (nm != nmem) return false;                 // by construction equal
+    if ((int32_t)threadIdx.x < nm) {
+        const uint64_t Pi = l.mP[threadIdx.x];
+        const uint64_t wi = l.mfw[threadIdx.x];
+        uint64_t ahead = before;
+        int32_t cnt = 0;
+        for (int32_t j = 0; j < nm; ++j)
+            if (l.mP[j] > Pi) {
+                ahead += l.mfw[j];
+                ++cnt;
+            }
+        if (ahead <= T0f && ahead + wi > T0f) {
+            l.res[0] = Pi;
+            l.res[1] = ahead + wi;
+            l.res[2] = (uint64_t)(cbefore + cnt + 1);
+        }
+    }
+    __syncthreads();
+
+    // D. publish: the kept list (order free), the draft token's probability,
+    // then the row descriptor
+    const uint64_t pmin = l.res[0];
+    if (pmin == 0) return false;                  // by construction found
+    const float Zk = (float)((double)l.res[1] / kFixW);
+    for (int32_t t0 = 0; t0 < n; t0 += NT) {
+        const int32_t t = t0 + (int32_t)threadIdx.x;
+        const uint64_t P = t < n ? l.P[t] : 0ull;
+        const bool in = t < n && P >= pmin;
+        const int32_t pos = wave_append(in, &l.cnt[2]);
+        if (in) {
+            const int32_t id = pid(P);
+            KeptEnt e;
+            e.id = id;
+            e.w = exp2_hw((fkey_inv(pkey(P)) - m) * c);
+            pub(&kept[pos], e);
+            if (xtok >= 0 && (d2t ? d2t[id] == xtok : id == xtok)) *l.ptok = e.w / Zk;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        RowDesc d;
+        d.m = m;
+        d.Z = Z;
+        d.Zk = Zk;
+        d.key = pkey(pmin);
+        d.tie_cut = pid(pmin);
+        d.nkept = (int32_t)l.res[2];
+        d.flags = RD_HAS_LIST;
+        d.ptok = *l.ptok;
+        pub(out, d);
+    }
+    return true;
+}
+
 template <int DT, int NT, int U>
 __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, float band, float top_p, RowDesc *out,
                                          KeptEnt *kept, uint64_t *s_lds, int32_t *s_cvid, int32_t xtok,
@@ -812,13 +1059,20 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
     __shared__ float s_mred[NT / kWave], s_sred[NT / kWave];
     __shared__ unsigned long long s_bmass[4], s_zk, s_pmin;
     __shared__ float s_ptok;
+    __shared__ int32_t s_bcnt[3];
+    __shared__ unsigned long long s_bres[3];
     uint64_t *s_cand = s_lds;                                          // [kCandCap] band tokens
     u32x4 *s_cvec = reinterpret_cast<u32x4 *>(s_lds + kCandCap);       // [kCandVecCap] band vectors
     uint64_t *s_P = s_lds + kCandCap;                                  // [kCandCap] after expansion
     uint32_t *s_fw = reinterpret_cast<uint32_t *>(s_lds + 2 * kCandCap);            // [kCandCap]
     uint64_t *s_ahead = s_lds + 2 * kCandCap + kCandCap / 2;                        // [NT] / radix bins
 
-    if (threadIdx.x == 0) { s_maxkey = fkey(-INFINITY); s_ncand = 0; s_nvec = 0; s_nlist = 0; }
+    if (threadIdx.x == 0) { s_maxkey = fkey(-INFINITY); s_ncand = 0; s_nvec = 0; s_nlist = 0; s_ptok = 0.0f; }
+    if (threadIdx.x < 3) { s_bcnt[threadIdx.x] = 0; s_bres[threadIdx.x] = 0; }
+    if (threadIdx.x < kWave) {                  // bin select: masses and counts
+        s_ahead[threadIdx.x] = 0;
+        reinterpret_cast<uint32_t *>(s_ahead + kWave)[threadIdx.x] = 0;
+    }
     __syncthreads();
 
     using E = Elem<DT>;
@@ -950,19 +1204,18 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
     MaxSum ms;
     ms.m = m_l;
     ms.s = s_l;
-    ms = wave_maxsum(ms, c);
+    ms = wave_maxsum_dpp(ms, c);
     if ((threadIdx.x & (kWave - 1)) == 0) { s_mred[threadIdx.x / kWave] = ms.m; s_sred[threadIdx.x / kWave] = ms.s; }
     __syncthreads();
-    MaxSum tot;
-    tot.m = s_mred[0];
-    tot.s = s_sred[0];
-    for (int w = 1; w < NT / kWave; ++w) {
-        MaxSum o;
-        o.m = s_mred[w];
-        o.s = s_sred[w];
-        tot = maxsum_merge(tot, o, c);
+    float m = s_mred[0];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) m = fmaxf(m, s_mred[w]);
+    float Z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        const float mw = s_mred[w];
+        if (mw > -INFINITY) Z += s_sred[w] * exp2_hw((mw - m) * c);
     }
-    const float m = tot.m, Z = tot.s;
     if (bad_max(m)) {
         if (threadIdx.x == 0) {
             RowDesc d;
@@ -973,9 +1226,28 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         return;
     }
 
-    // ---- expand the band: every token with z >= m - band ----
     const float thr_final = m - band;
     const int32_t nvc = s_nvec;
+    // ---- usual case: select by bins ----
+    if (nvc <= kCandVecCap) {
+        BinSelectLds l;
+        l.P = s_cand;
+        l.fw = s_fw;
+        l.bm = s_ahead;
+        l.bc = reinterpret_cast<uint32_t *>(s_ahead + kWave);
+        l.mP = s_ahead + kWave + kWave / 2;
+        l.mfw = reinterpret_cast<uint32_t *>(l.mP + kBinMembers);
+        l.cnt = s_bcnt;
+        l.res = reinterpret_cast<uint64_t *>(s_bres);
+        l.ptok = &s_ptok;
+        static_assert(kWave + kWave / 2 + kBinMembers + kBinMembers / 2 <= 512, "bins fit the pairwise area");
+        static_assert(kCandCap + 2 * kCandVecCap <= 2 * kCandCap, "band vectors stay clear of the token lists");
+        if (bin_select<DT, NT>(row, sp, L, nvc, s_cvec, s_cvid, l, m, Z, c, band, top_p, xtok, d2t, out, kept))
+            return;
+        __syncthreads();      // the general path below reuses what the bin select wrote
+    }
+
+    // ---- expand the band: every token with z >= m - band ----
     bool fallback = nvc > kCandVecCap;
     if (!fallback) {
         // called by every lane of every wave (wave-aggregated append)
@@ -1328,6 +1600,86 @@ __device__ SV_RARE int32_t draw_full_row(const SampleArgs &a, int32_t b, int32_t
     return tok;
 }
 
+// The draw of draw_from_list when both kept lists are in LDS with at most
+// kWave entries each, for 512-thread workgroups: p's entry i is handled by
+// the 8 threads of one half-row (threads 8i .. 8i+7), thread s of them taking
+// every 8th entry from s of the other list; their parts combine by DPP inside
+// the half-row.  Two workgroup barriers (three with a d2t map).  The
+// arithmetic is that of draw_from_list, so both give the same token.
+__device__ __forceinline__ float half_row_sum_f32(float v) {
+    v = dpp_add_f32<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
+    v = dpp_add_f32<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
+    v = dpp_add_f32<0x141, 0xf>(v);    // row_half_mirror
+    return v;
+}
+__device__ __forceinline__ uint64_t half_row_sum_u64(uint64_t v) {
+    v = dpp_add_u64<0xB1, 0xf>(v);
+    v = dpp_add_u64<0x4E, 0xf>(v);
+    v = dpp_add_u64<0x141, 0xf>(v);
+    return v;
+}
+
+template <int NT>
+__device__ __forceinline__ int32_t group_draw_list(const SampleArgs &a, const RowDesc &dp, const RowDesc &dq,
+                                                   bool resid, const KeptEnt *pl, const KeptEnt *pq, double u,
+                                                   uint64_t *s_rf, int32_t *s_id, int32_t *s_qid, int32_t *s_tok) {
+    constexpr int G = 8;
+    static_assert(NT == G * kWave, "one half-row per entry of a 64-entry list");
+    const int32_t i = threadIdx.x / G, sl = threadIdx.x % G;
+    const int32_t K = dp.nkept, Kq = resid ? dq.nkept : 0;
+    const bool has = i < K;
+    KeptEnt e;
+    e.id = INT32_MAX;
+    e.w = 0.0f;
+    if (has) e = pl[i];
+    if (threadIdx.x == 0) *s_tok = -1;
+    if (a.d2t && Kq > 0) {
+        // q's entries carry draft ids: their target ids once, in LDS
+        if ((int32_t)threadIdx.x < Kq) s_qid[threadIdx.x] = a.d2t[pq[threadIdx.x].id];
+        __syncthreads();
+    }
+    // q of entry i: at most one of q's entries has its id (ids are distinct)
+    float qpart = 0.0f;
+    if (has)
+        for (int32_t j = sl; j < Kq; j += G) {
+            const KeptEnt qe = pq[j];
+            const int32_t qid = a.d2t ? s_qid[j] : qe.id;
+            if (qid == e.id) qpart = qe.w / dq.Zk;
+        }
+    const float q = half_row_sum_f32(qpart);
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        const bool use_resid = resid && attempt == 0;
+        float r = e.w / dp.Zk;
+        if (use_resid) r = r - q > 0.0f ? r - q : 0.0f;
+        const uint64_t rf = has ? (uint64_t)((double)r * kFixW) : 0ull;
+        if (sl == 0) {
+            s_rf[i] = rf;
+            s_id[i] = e.id;
+        }
+        __syncthreads();
+        // mass of the entries with id <= this entry's, and the total
+        uint64_t inc = 0, S = 0;
+        for (int32_t j = sl; j < K; j += G) {
+            const uint64_t rj = s_rf[j];
+            S += rj;
+            if (s_id[j] <= e.id) inc += rj;
+        }
+        inc = half_row_sum_u64(inc);
+        S = half_row_sum_u64(S);
+        if (S > 0) {
+            // exactly one entry (in id order) brackets the target
+            const uint64_t target = (uint64_t)(u * (double)S);
+            if (has && sl == 0 && rf > 0 && inc > target && inc - rf <= target) *s_tok = e.id;
+            __syncthreads();
+            return *s_tok;
+        }
+        if (!use_resid) return -1;
+        // zero residual mass (only with p == q on p's support): draw from p_n
+        __syncthreads();
+    }
+    return -1;
+}
+
 // Kept-list prefixes staged by the sequence epilogue, at the end of the
 // band area (past what the draws use).
 constexpr int kPreBase = 4096;                 // u64 offset in the band area
@@ -1355,7 +1707,6 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     __shared__ int last_flag;
     __shared__ int32_t s_itmp[NT / kWave];
     __shared__ double s_dtmp[NT / kWave];
-    __shared__ int32_t s_status;
     __shared__ int32_t s_j[2];
 
     const int32_t g = a.gamma, NR = 2 * g + 1;
@@ -1386,12 +1737,14 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     if (!arrive_last(&a.cnt_stats[b], (uint32_t)NR, &last_flag)) return;
 
     // ---- sequence epilogue: accept chain, then the draw ----
-    // one round of loads: the row descriptors, this thread's draft position
-    // (token, uniform) and the sampling uniform
+    // one round of loads: the row descriptors, the kept-list prefixes, each
+    // wave's copy of the first kWave draft positions (token, uniform) and the
+    // sampling uniform
     RowDesc *s_rows = reinterpret_cast<RowDesc *>(s_cand);   // the row work is done
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int32_t *x = a.tokens + (size_t)b * g;
-    const int32_t ti = (int32_t)threadIdx.x < g ? x[threadIdx.x] : 0;
-    const double ui = (int32_t)threadIdx.x < g ? (double)a.u_acc[(size_t)b * g + threadIdx.x] : 0.0;
+    const int32_t ti = lane < g ? x[lane] : 0;
+    const double ui = lane < g ? (double)a.u_acc[(size_t)b * g + lane] : 0.0;
     const double u = (double)a.u_s[b];
     for (int32_t k = threadIdx.x; k < NR; k += NT) s_rows[k] = sub(&rows[k]);
     // the first kPre entries of every row's kept list, loaded in the same
@@ -1400,46 +1753,82 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     const int32_t kPre = min(kPreMax, kPreSlots / NR);
     for (int32_t e = threadIdx.x; e < NR * kPre; e += NT)
         s_pre[e] = sub(&a.kept[((size_t)b * NR + e / kPre) * a.kept_stride + min(e % kPre, a.kept_stride - 1)]);
-    if (threadIdx.x == 0) s_status = 0;
     __syncthreads();
-    for (int32_t k = threadIdx.x; k < NR; k += NT)
-        if (s_rows[k].flags & RD_NO_MASS) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
-    int32_t n;
+    // Status and chain, in every wave alike (so that all waves take the same
+    // branch below): every row has published the probability of its own
+    // draft token; n is the first position where u * q < p fails.
+    int32_t status = 0, n = g;
     {
-        // every row has published the probability of its own draft token
-        static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
-        const int32_t i = threadIdx.x;
-        int32_t first_rej = INT32_MAX;
-        if (i < g) {
-            if (ti < 0 || ti >= a.Vt) atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
-            const float pa = s_rows[i].ptok, qc = s_rows[g + 1 + i].ptok;
-            if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
-            if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
-            if (!(ui * (double)qc < (double)pa)) first_rej = i;
+        uint64_t nomass = 0;
+        for (int32_t k0 = 0; k0 < NR; k0 += kWave) {
+            const int32_t k = k0 + lane;
+            nomass |= __ballot(k < NR && (s_rows[k].flags & RD_NO_MASS) != 0);
         }
-        const int32_t fr = wg_min_i32<NT>(first_rej, s_itmp);
-        n = fr == INT32_MAX ? g : fr;
-        if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? ti : -1;
+        if (nomass) status |= SV_SEQ_NO_MASS;
+        for (int32_t i0 = 0; i0 < g; i0 += kWave) {
+            const int32_t i = i0 + lane;
+            int32_t t = ti;
+            double uu = ui;
+            if (i0 > 0) {                                   // more than kWave drafts (rare)
+                t = i < g ? x[i] : 0;
+                uu = i < g ? (double)a.u_acc[(size_t)b * g + i] : 0.0;
+            }
+            bool bad = false, rej = false;
+            if (i < g) {
+                bad = t < 0 || t >= a.Vt;
+                const float pa = s_rows[i].ptok, qc = s_rows[g + 1 + i].ptok;
+                if (wv == 0) {
+                    if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
+                    if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
+                }
+                rej = !(uu * (double)qc < (double)pa);
+            }
+            if (__ballot(bad)) status |= SV_SEQ_TOKEN_RANGE;
+            const uint64_t rb = __ballot(rej);
+            if (rb && n == g) n = i0 + __ffsll((unsigned long long)rb) - 1;
+        }
+        if (wv == 0)
+            for (int32_t i0 = 0; i0 <= g; i0 += kWave) {
+                const int32_t i = i0 + lane;
+                if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? (i0 == 0 ? ti : x[i]) : -1;
+            }
     }
     const RowDesc dp = s_rows[n];
     const RowDesc dq = n < g ? s_rows[g + 1 + n] : dp;
+    int32_t tok = -1;
+    const bool short_lists = (dp.flags & RD_HAS_LIST) && dp.nkept <= kPre && dp.nkept <= kWave &&
+                             (n == g || ((dq.flags & RD_HAS_LIST) && dq.nkept <= kPre && dq.nkept <= kWave));
     __syncthreads();                                          // s_rows is reused below
-    int32_t tok;
-    if (dp.flags & RD_HAS_LIST) {
-        const KeptEnt *pl = dp.nkept <= kPre ? s_pre + (size_t)n * kPre : nullptr;
-        const KeptEnt *pq = (n < g && dq.nkept <= kPre) ? s_pre + (size_t)(g + 1 + n) * kPre : nullptr;
-        tok = draw_from_list<DTT, DTD, NT>(a, b, n, dp, dq, a.kept + ((size_t)b * NR + n) * a.kept_stride,
-                                           a.kept + ((size_t)b * NR + g + 1 + n) * a.kept_stride, pl, pq, s_cand, u,
-                                           s_dtmp, s_itmp);
-    } else {
-        // kept set too large for a list: tile-by-tile over the whole row
-        tok = draw_full_row<DTT, DTD, NT>(a, b, n, dp, dq, u, reinterpret_cast<float *>(s_cand), s_dtmp, s_itmp,
-                                          s_j);
+    bool drawn = false;
+    if constexpr (NT == 8 * kWave) {
+        if (short_lists) {
+            // usual case: both lists are in LDS with at most kWave entries
+            uint64_t *s_rf = s_cand;                                         // [kWave]
+            int32_t *s_id = reinterpret_cast<int32_t *>(s_cand + kWave);     // [kWave]
+            int32_t *s_qid = s_id + kWave;                                   // [kWave]
+            static_assert(kWave + kWave <= kPreBase, "draw scratch stays below the list prefixes");
+            tok = group_draw_list<NT>(a, dp, dq, n < g, s_pre + (size_t)n * kPre,
+                                      s_pre + (size_t)(n < g ? g + 1 + n : n) * kPre, u, s_rf, s_id, s_qid, &s_j[0]);
+            drawn = true;
+        }
+    }
+    if (!drawn) {
+        if (dp.flags & RD_HAS_LIST) {
+            const KeptEnt *pl = dp.nkept <= kPre ? s_pre + (size_t)n * kPre : nullptr;
+            const KeptEnt *pq = (n < g && dq.nkept <= kPre) ? s_pre + (size_t)(g + 1 + n) * kPre : nullptr;
+            tok = draw_from_list<DTT, DTD, NT>(a, b, n, dp, dq, a.kept + ((size_t)b * NR + n) * a.kept_stride,
+                                               a.kept + ((size_t)b * NR + g + 1 + n) * a.kept_stride, pl, pq, s_cand,
+                                               u, s_dtmp, s_itmp);
+        } else {
+            // kept set too large for a list: tile-by-tile over the whole row
+            tok = draw_full_row<DTT, DTD, NT>(a, b, n, dp, dq, u, reinterpret_cast<float *>(s_cand), s_dtmp, s_itmp,
+                                              s_j);
+        }
     }
     if (threadIdx.x == 0) {
         a.out_tokens[(size_t)b * (g + 1) + n] = tok;
         a.out_len[b] = n;
-        if (a.out_status) a.out_status[b] = s_status;
+        if (a.out_status) a.out_status[b] = status;
     }
 }
 
@@ -1715,42 +2104,6 @@ __device__ __forceinline__ uint64_t fix52(float w) {
     const int sh = (e ? e : 1) - 98;                 // w = m * 2^(e - 150), times 2^52
     if (sh >= 0) return m << sh;
     return sh > -24 ? m >> -sh : 0;
-}
-
-// One step of a wave reduction on a 64-bit value: add the value DPP-moved
-// under control CTRL (rows outside ROWMASK add 0).  No LDS traffic.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t dpp_add_u64(uint64_t v) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
-    return v + (((uint64_t)hi << 32) | lo);
-}
-// Sum over the 64 lanes, returned to every lane (all lanes must be active):
-// pairs, quads, half rows and rows by DPP permutes, then the rows are
-// chained through the row broadcasts so that lane 63 holds the total.
-__device__ __forceinline__ uint64_t wave_total_u64(uint64_t v) {
-    v = dpp_add_u64<0xB1, 0xf>(v);     // quad_perm [1,0,3,2]
-    v = dpp_add_u64<0x4E, 0xf>(v);     // quad_perm [2,3,0,1]
-    v = dpp_add_u64<0x141, 0xf>(v);    // row_half_mirror
-    v = dpp_add_u64<0x140, 0xf>(v);    // row_mirror
-    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
-    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Inclusive prefix sum over the 64 lanes in lane order (all lanes active):
-// shifts by 1, 2, 4, 8 inside each row of 16, then the row totals are carried
-// through the row broadcasts.
-__device__ __forceinline__ uint64_t wave_incl_scan_u64_dpp(uint64_t v) {
-    v = dpp_add_u64<0x111, 0xf>(v);    // row_shr:1
-    v = dpp_add_u64<0x112, 0xf>(v);    // row_shr:2
-    v = dpp_add_u64<0x114, 0xf>(v);    // row_shr:4
-    v = dpp_add_u64<0x118, 0xf>(v);    // row_shr:8
-    v = dpp_add_u64<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
-    v = dpp_add_u64<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
-    return v;
 }
 
 // floor(u * S) exactly, for a float32 u in [0, 1).
