@@ -73,7 +73,6 @@ constexpr int kQListCap = 1024;     // q lists up to this size are matched in LD
 constexpr int kTile = 4096;         // most target ids per residual/bonus tile
 constexpr int kTileMin = 1024;      // fewest (tiles shrink for small batches)
 constexpr int kDrawMinWgs = 512;    // tiles shrink until the draw has this many workgroups
-constexpr int kDrawGroup = 8;       // draw tiles per first-level arrival counter
 #ifndef SV_STATS_MIN_WGS
 #define SV_STATS_MIN_WGS 256
 #endif
@@ -158,8 +157,7 @@ struct SampleArgs {
     int32_t *out_tokens, *out_len, *out_status;
     float *out_p, *out_q;
     // workspace
-    uint32_t *cnt_stats;       // [B]
-    uint32_t *cnt_draw;        // [B, 1 + ceil(ntiles / kDrawGroup)]
+    uint32_t *cnt_stats;       // [B] (top-p)
     SeqState *seq;             // [B]
     RowDesc *rows;             // [B, 2*gamma+1]: target rows then draft rows
     MaxSum *part;              // [B, (gamma+1)*Ct + gamma*Cd]
@@ -189,7 +187,7 @@ inline bool workspace_fits(size_t W, size_t counter_bytes, size_t data_bytes) {
 }
 
 struct WorkspaceLayout {
-    size_t cnt_stats, cnt_draw, counter_bytes;               // offsets from 0
+    size_t cnt_stats, counter_bytes;                         // offsets from 0
     size_t seq, rows, part, kept, probe, tile_mass, tile_jb, data_bytes;   // offsets from K
 };
 // Workspace layout and launch shape of one sampling call; bt / bd are the

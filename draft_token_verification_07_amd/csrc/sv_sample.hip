@@ -1931,7 +1931,7 @@ __device__ __forceinline__ void probe_tokens_g(const SampleArgs &a, int32_t b) {
         } else if (valid && gl == 0) {
             pr.zd = ld_logit<DTD>(drow, t);
         }
-        if (has && gl == 0) pub(&a.probe[(size_t)b * g + i], pr);
+        if (has && gl == 0) a.probe[(size_t)b * g + i] = pr;
     }
 }
 
@@ -1965,122 +1965,38 @@ __device__ __forceinline__ void tile_bounds(const SampleArgs &a, int32_t b) {
     }
 }
 
-// Grid: B probe workgroups, then B * ((gamma+1) * Ct + gamma * Cd) chunk
-// workgroups.  The last of a sequence's workgroups merges the chunk partials
-// of every row, runs the accept chain and records n for the draw.
+// Plain mode, first launch.  Grid: B probe workgroups, then
+// B * ((gamma+1) * Ct + gamma * Cd) chunk workgroups; each chunk workgroup
+// writes the (max, sum) of its chunk, each probe workgroup the logits at the
+// draft tokens (and, with d2t, its share of the tile boundaries).  The next
+// launch merges them.
 template <int DTT, int DTD, int NT, int U>
 __global__ __launch_bounds__(NT) void stats_kernel(SampleArgs a) {
-    static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
     __shared__ float s_m[NT / kWave], s_s[NT / kWave];
-    __shared__ MaxSum s_part[kPartCap];
-    extern __shared__ RowDesc s_rows[];                       // [2 * gamma + 1]
-    __shared__ int last_flag;
-    __shared__ int32_t s_itmp[NT / kWave];
-    __shared__ int32_t s_status;
-
-    const int32_t g = a.gamma, NR = 2 * g + 1;
+    const int32_t g = a.gamma;
     const int32_t per_seq = (g + 1) * a.Ct + g * a.Cd;
-    int32_t b, w;
     if ((int32_t)blockIdx.x < a.B) {
-        b = blockIdx.x;
-        w = -1;
-    } else {
-        b = ((int32_t)blockIdx.x - a.B) / per_seq;
-        w = ((int32_t)blockIdx.x - a.B) % per_seq;
-    }
-    MaxSum *part = a.part + (size_t)b * per_seq;
-    if (w < 0) {
+        const int32_t b = blockIdx.x;
         probe_tokens<DTT, DTD, NT>(a, b);
         if (a.d2t) tile_bounds<NT>(a, b);
+        return;
+    }
+    const int32_t b = ((int32_t)blockIdx.x - a.B) / per_seq;
+    const int32_t w = ((int32_t)blockIdx.x - a.B) % per_seq;
+    MaxSum ms;
+    if (w < (g + 1) * a.Ct) {
+        const int32_t r = w / a.Ct, ch = w % a.Ct;
+        const void *row = reinterpret_cast<const char *>(a.tl) +
+                          ((size_t)b * (g + 1) + r) * (size_t)a.Vt * Elem<DTT>::kBytes;
+        ms = chunk_maxsum<DTT, NT, U>(row, a.Vt, ch, a.Ct, a.c, s_m, s_s);
     } else {
-        MaxSum ms;
-        if (w < (g + 1) * a.Ct) {
-            const int32_t r = w / a.Ct, ch = w % a.Ct;
-            const void *row = reinterpret_cast<const char *>(a.tl) +
-                              ((size_t)b * (g + 1) + r) * (size_t)a.Vt * Elem<DTT>::kBytes;
-            ms = chunk_maxsum<DTT, NT, U>(row, a.Vt, ch, a.Ct, a.c, s_m, s_s);
-        } else {
-            const int32_t w2 = w - (g + 1) * a.Ct;
-            const int32_t r = w2 / a.Cd, ch = w2 % a.Cd;
-            const void *row = reinterpret_cast<const char *>(a.dl) +
-                              ((size_t)b * g + r) * (size_t)a.Vd * Elem<DTD>::kBytes;
-            ms = chunk_maxsum<DTD, NT, U>(row, a.Vd, ch, a.Cd, a.c, s_m, s_s);
-        }
-        if (threadIdx.x == 0) pub(&part[w], ms);
+        const int32_t w2 = w - (g + 1) * a.Ct;
+        const int32_t r = w2 / a.Cd, ch = w2 % a.Cd;
+        const void *row = reinterpret_cast<const char *>(a.dl) +
+                          ((size_t)b * g + r) * (size_t)a.Vd * Elem<DTD>::kBytes;
+        ms = chunk_maxsum<DTD, NT, U>(row, a.Vd, ch, a.Cd, a.c, s_m, s_s);
     }
-
-    if (!arrive_last(&a.cnt_stats[b], (uint32_t)per_seq + 1u, &last_flag)) return;
-
-    // one round of loads: the chunk partials (into LDS), and this thread's
-    // draft position (token, probe, uniform)
-    if (threadIdx.x == 0) s_status = 0;
-    const bool staged = per_seq <= kPartCap;
-    if (staged)
-        for (int32_t k = threadIdx.x; k < per_seq; k += NT) s_part[k] = sub(&part[k]);
-    const int32_t i = threadIdx.x;
-    int32_t t = -1;
-    Probe pr;
-    pr.zt = 0.0f;
-    pr.zd = -INFINITY;
-    double ua = 0.0;
-    if (i < g) {
-        t = a.tokens[(size_t)b * g + i];
-        pr = sub(&a.probe[(size_t)b * g + i]);
-        ua = (double)a.u_acc[(size_t)b * g + i];
-    }
-    __syncthreads();
-    // row r is merged by thread r, chunk by chunk in order (identical rows
-    // give identical results)
-    for (int32_t r = threadIdx.x; r < NR; r += NT) {
-        const bool tgt = r <= g;
-        const int32_t C = tgt ? a.Ct : a.Cd;
-        const int32_t off = tgt ? r * a.Ct : (g + 1) * a.Ct + (r - g - 1) * a.Cd;
-        MaxSum acc = staged ? s_part[off] : sub(&part[off]);
-        for (int32_t k = 1; k < C; ++k) acc = maxsum_merge(acc, staged ? s_part[off + k] : sub(&part[off + k]), a.c);
-        {
-            RowDesc d;
-            d.m = acc.m;
-            d.Z = acc.s;
-            d.Zk = acc.s;
-            d.key = 0u;
-            d.tie_cut = INT32_MAX;
-            d.nkept = tgt ? a.Vt : a.Vd;
-            d.flags = bad_max(acc.m) ? RD_NO_MASS : 0;
-            d.ptok = 0.0f;
-            if (d.flags & RD_NO_MASS) atomicOr(&s_status, (int)SV_SEQ_NO_MASS);
-            s_rows[r] = d;
-            a.rows[(size_t)b * NR + r] = d;
-        }
-    }
-    __syncthreads();
-    int32_t first_rej = INT32_MAX;
-    if (i < g) {
-        float pa = 0.0f, qc = 0.0f;
-        if (t < 0 || t >= a.Vt) {
-            atomicOr(&s_status, (int)SV_SEQ_TOKEN_RANGE);
-        } else {
-            pa = row_prob(s_rows[i], pr.zt, t, a.c);
-            qc = row_prob(s_rows[g + 1 + i], pr.zd, t, a.c);
-        }
-        if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
-        if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
-        // u * q < p, exactly: both products fit a double
-        if (!(ua * (double)qc < (double)pa)) first_rej = i;
-    }
-    const int32_t fr = wg_min_i32<NT>(first_rej, s_itmp);
-    const int32_t n = fr == INT32_MAX ? g : fr;
-    if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? t : -1;
-    if (threadIdx.x == 0) {
-        SeqState st;
-        st.n = n;
-        st.status = s_status;
-        st.pad0 = st.pad1 = 0;
-        st.dp = s_rows[n];
-        st.dq = s_rows[n < g ? g + 1 + n : n];
-        a.seq[b] = st;
-        a.out_len[b] = n;
-        if (a.out_status) a.out_status[b] = s_status;
-    }
+    if (threadIdx.x == 0) a.part[(size_t)b * per_seq + w] = ms;
 }
 
 // ---------------------------------------------------------------------------
@@ -2207,12 +2123,11 @@ struct DrawTile {
 
 template <int DTT, int DTD, int NT>
 __device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const SampleArgs &a, int32_t b,
-                                               int32_t n, const SeqState *st, int32_t k, int32_t j0, int32_t j1,
-                                               float *s_q) {
+                                               int32_t n, const RowDesc &dp, const RowDesc &dq, int32_t k,
+                                               int32_t j0, int32_t j1, float *s_q) {
     using ET = Elem<DTT>;
     using ED = Elem<DTD>;
     const int32_t g = a.gamma;
-    const RowDesc dp = load_desc(&st->dp), dq = load_desc(&st->dq);
     x.trow = reinterpret_cast<const char *>(a.tl) + ((size_t)b * (g + 1) + n) * (size_t)a.Vt * ET::kBytes;
     x.drow = n < g ? reinterpret_cast<const char *>(a.dl) + ((size_t)b * g + n) * (size_t)a.Vd * ED::kBytes
                    : nullptr;
@@ -2282,8 +2197,147 @@ __device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const 
     }
 }
 
+// Plain mode, second launch.  Grid: B * ntiles.  Workgroup (b, k) merges the
+// chunk statistics of sequence b in chunk order (every workgroup of b alike),
+// runs the accept chain, and sums the fixed-point residual (or bonus)
+// weights of target tile k of row n.  Workgroup (b, 0) also writes the
+// accepted tokens, the probabilities, the status and the sequence state.
 template <int DTT, int DTD, int NT>
-__global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
+__global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
+    using DT = DrawTile<DTT, DTD, NT>;
+    constexpr int U = DT::U;
+    constexpr int NW = NT / kWave;
+    static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
+    extern __shared__ RowDesc s_rows[];                       // [2 * gamma + 1]
+    __shared__ MaxSum s_part[kPartCap];
+    __shared__ float s_q[kTile];
+    __shared__ uint64_t s_tmp[NW];
+
+    const int32_t g = a.gamma, NR = 2 * g + 1;
+    const int32_t per_seq = (g + 1) * a.Ct + g * a.Cd;
+    const int32_t b = blockIdx.x / a.ntiles, k = blockIdx.x % a.ntiles;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+
+    // one round of loads: the chunk partials (into LDS), this thread's draft
+    // position (token, probe, uniform), the tile's draft-id range
+    const MaxSum *part = a.part + (size_t)b * per_seq;
+    const bool staged = per_seq <= kPartCap;
+    if (staged)
+        for (int32_t q = threadIdx.x; q < per_seq; q += NT) s_part[q] = part[q];
+    const int32_t i = threadIdx.x;
+    int32_t t = -1;
+    Probe pr;
+    pr.zt = 0.0f;
+    pr.zd = -INFINITY;
+    double ua = 0.0;
+    if (i < g) {
+        t = a.tokens[(size_t)b * g + i];
+        pr = a.probe[(size_t)b * g + i];
+        ua = (double)a.u_acc[(size_t)b * g + i];
+    }
+    int32_t j0 = 0, j1 = 0;
+    if (a.d2t) {
+        j0 = min(max(a.tile_jb[k], 0), a.Vd);
+        j1 = min(max(a.tile_jb[k + 1], j0), a.Vd);
+    }
+    __syncthreads();
+    // row r is merged by thread r, chunk by chunk in order (identical rows
+    // give identical results)
+    for (int32_t r = threadIdx.x; r < NR; r += NT) {
+        const bool tgt = r <= g;
+        const int32_t C = tgt ? a.Ct : a.Cd;
+        const int32_t off = tgt ? r * a.Ct : (g + 1) * a.Ct + (r - g - 1) * a.Cd;
+        MaxSum acc = staged ? s_part[off] : part[off];
+        for (int32_t q = 1; q < C; ++q) acc = maxsum_merge(acc, staged ? s_part[off + q] : part[off + q], a.c);
+        RowDesc d;
+        d.m = acc.m;
+        d.Z = acc.s;
+        d.Zk = acc.s;
+        d.key = 0u;
+        d.tie_cut = INT32_MAX;
+        d.nkept = tgt ? a.Vt : a.Vd;
+        d.flags = bad_max(acc.m) ? RD_NO_MASS : 0;
+        d.ptok = 0.0f;
+        s_rows[r] = d;
+    }
+    __syncthreads();
+    // the chain: n is the first position where u * q < p fails (exactly:
+    // both products fit a double)
+    float pa = 0.0f, qc = 0.0f;
+    bool bad = false, rej = false;
+    if (i < g) {
+        if (t < 0 || t >= a.Vt) {
+            bad = true;
+        } else {
+            pa = row_prob(s_rows[i], pr.zt, t, a.c);
+            qc = row_prob(s_rows[g + 1 + i], pr.zd, t, a.c);
+        }
+        rej = !(ua * (double)qc < (double)pa);
+    }
+    int32_t n;
+    {
+        // positions 0..g-1 live in the first waves; every wave reads them from LDS
+        __shared__ unsigned long long s_rej[(SV_MAX_GAMMA + kWave) / kWave];
+        __shared__ int s_flags;
+        if (threadIdx.x == 0) s_flags = 0;
+        const uint64_t rb = __ballot(rej);
+        if (lane == 0 && wv * kWave < g) s_rej[wv] = rb;
+        __syncthreads();
+        if (bad) atomicOr(&s_flags, 1);
+        n = g;
+        for (int w = 0; w * kWave < g; ++w)
+            if (s_rej[w]) {
+                n = w * kWave + __ffsll(s_rej[w]) - 1;
+                break;
+            }
+        if (k == 0) {
+            if (i < g) {
+                if (a.out_p) a.out_p[(size_t)b * g + i] = pa;
+                if (a.out_q) a.out_q[(size_t)b * g + i] = qc;
+            }
+            if (i <= g && i != n) a.out_tokens[(size_t)b * (g + 1) + i] = i < n ? t : -1;
+        }
+        __syncthreads();
+        if (k == 0 && threadIdx.x == 0) {
+            int32_t status = (s_flags & 1) ? SV_SEQ_TOKEN_RANGE : 0;
+            for (int32_t r = 0; r < NR; ++r)
+                if (s_rows[r].flags & RD_NO_MASS) status |= SV_SEQ_NO_MASS;
+            SeqState st;
+            st.n = n;
+            st.status = status;
+            st.pad0 = st.pad1 = 0;
+            st.dp = s_rows[n];
+            st.dq = s_rows[n < g ? g + 1 + n : n];
+            a.seq[b] = st;
+            a.out_len[b] = n;
+            if (a.out_status) a.out_status[b] = status;
+        }
+    }
+    const RowDesc dp = s_rows[n];
+    const RowDesc dq = n < g ? s_rows[g + 1 + n] : dp;
+    DT x;
+    draw_tile_load<DTT, DTD, NT>(x, a, b, n, dp, dq, k, j0, j1, s_q);
+    auto none = [](int32_t, uint64_t) {};
+    uint64_t sm = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm += x.slice(u, s_q, none);
+    const int32_t te = x.edge_id();
+    if (te >= 0) sm += x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q));
+    sm = wave_total_u64(sm);
+    if (lane == 0) s_tmp[wv] = sm;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t mass = 0;
+        for (int w = 0; w < NW; ++w) mass += s_tmp[w];
+        a.tile_mass[(size_t)b * a.ntiles + k] = mass;
+    }
+}
+
+// Plain mode, third launch.  Grid: B.  Workgroup b picks the tile holding
+// floor(u * S) from the tile masses, reloads it and finds the token inside
+// (exact fixed-point sums, so the pick and the search agree).
+template <int DTT, int DTD, int NT>
+__global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
     using DT = DrawTile<DTT, DTD, NT>;
     constexpr int U = DT::U;
     constexpr int NW = NT / kWave;
@@ -2293,53 +2347,19 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
     __shared__ uint64_t s_pick[2];
     __shared__ int32_t s_jr[2];
     __shared__ int32_t s_tok;
-    __shared__ int last_flag;
     // rare fallback (zero residual mass)
     __shared__ double s_dtmp[NW];
     __shared__ int32_t s_itmp[NW];
     __shared__ int32_t s_j[2];
 
     const int32_t g = a.gamma;
-    const int32_t b = blockIdx.x / a.ntiles, k = blockIdx.x % a.ntiles;
+    const int32_t b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const SeqState *st = &a.seq[b];
     const int32_t n = st->n;
-    int32_t j0 = 0, j1 = 0;
-    if (a.d2t) {
-        j0 = min(max(a.tile_jb[k], 0), a.Vd);
-        j1 = min(max(a.tile_jb[k + 1], j0), a.Vd);
-    }
+    const RowDesc dp = load_desc(&st->dp), dq = load_desc(&st->dq);
+    const uint64_t *mass = a.tile_mass + (size_t)b * a.ntiles;
     DT x;
-    draw_tile_load<DTT, DTD, NT>(x, a, b, n, st, k, j0, j1, s_q);
-    uint64_t *mass = a.tile_mass + (size_t)b * a.ntiles;
-    {
-        auto none = [](int32_t, uint64_t) {};
-        uint64_t s = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) s += x.slice(u, s_q, none);
-        const int32_t te = x.edge_id();
-        if (te >= 0) s += x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q));
-        s = wave_total_u64(s);
-        if (lane == 0) s_tmp[wv] = s;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint64_t m = 0;
-            for (int w = 0; w < NW; ++w) m += s_tmp[w];
-            pub_u64(&mass[k], m);
-        }
-    }
-
-    // two-level arrival: tiles of a sequence finish together, and one counter
-    // taking all of their atomics at once would serialize them
-    {
-        const int32_t ng = (a.ntiles + kDrawGroup - 1) / kDrawGroup;
-        uint32_t *cnt = a.cnt_draw + (size_t)b * (ng + 1);
-        const int32_t grp = k / kDrawGroup;
-        const uint32_t gsz = (uint32_t)min(kDrawGroup, a.ntiles - grp * kDrawGroup);
-        if (!arrive_last(&cnt[1 + grp], gsz, &last_flag)) return;
-        if (ng > 1 && !arrive_last(&cnt[0], (uint32_t)ng, &last_flag)) return;
-    }
-
     const float u_s = a.u_s[b];
     // S and the tile holding floor(u * S): one round of loads when the tiles
     // fit one per thread (else a first sweep for S, a second for the pick)
@@ -2349,7 +2369,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
     int32_t jr0 = 0, jr1 = 0;
     for (int32_t r = 0; r < rounds; ++r) {
         const int32_t kk = r * NT + (int32_t)threadIdx.x;
-        const uint64_t mk = kk < a.ntiles ? sub_u64(&mass[kk]) : 0;
+        const uint64_t mk = kk < a.ntiles ? mass[kk] : 0;
         if (r == 0) {
             mk0 = mk;
             if (a.d2t && kk < a.ntiles) {
@@ -2370,7 +2390,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
         uint64_t run = 0;
         for (int32_t r = 0; r < rounds; ++r) {
             const int32_t kk = r * NT + (int32_t)threadIdx.x;
-            const uint64_t mk = r == 0 ? mk0 : (kk < a.ntiles ? sub_u64(&mass[kk]) : 0);
+            const uint64_t mk = r == 0 ? mk0 : (kk < a.ntiles ? mass[kk] : 0);
             const uint64_t inc = wave_incl_scan_u64_dpp(mk);
             if (lane == kWave - 1) s_tmp[wv] = inc;
             __syncthreads();
@@ -2400,7 +2420,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
             const uint64_t tin = s_pick[1];
             const int32_t pj0 = a.d2t ? s_jr[0] : 0, pj1 = a.d2t ? s_jr[1] : 0;
             __syncthreads();
-            draw_tile_load<DTT, DTD, NT>(x, a, b, n, st, kp, pj0, pj1, s_q);
+            draw_tile_load<DTT, DTD, NT>(x, a, b, n, dp, dq, kp, pj0, pj1, s_q);
             // order of the tile's ids: the head ids, the slices (thread order
             // inside each), the tail ids.  Each wave puts its slice totals in
             // LDS; every thread then finds the block holding tin by itself.
@@ -2494,11 +2514,11 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
     } else if (n < g) {
         // zero residual mass (p == q wherever p > 0): draw from p_n itself
         DrawCtx y;
-        y.trow = x.trow;
-        y.drow = x.drow;
+        y.trow = reinterpret_cast<const char *>(a.tl) + ((size_t)b * (g + 1) + n) * (size_t)a.Vt * Elem<DTT>::kBytes;
+        y.drow = reinterpret_cast<const char *>(a.dl) + ((size_t)b * g + n) * (size_t)a.Vd * Elem<DTD>::kBytes;
         y.d2t = nullptr;
         y.Vd = a.Vd;
-        y.dp = load_desc(&st->dp);
+        y.dp = dp;
         y.dq = y.dp;
         y.c = a.c;
         y.resid = false;
@@ -2506,6 +2526,7 @@ __global__ __launch_bounds__(NT) void draw_kernel(SampleArgs a) {
     }
     if (threadIdx.x == 0) a.out_tokens[(size_t)b * (g + 1) + n] = tok;
 }
+
 
 // ---------------------------------------------------------------------------
 // Host side: workspace layout and launches
@@ -2551,9 +2572,7 @@ bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt,
     const int32_t tl = draw_tile(B, Vt);
     const int32_t nt = (Vt + tl - 1) / tl;
     L->cnt_stats = 0;
-    L->cnt_draw = align256(sizeof(uint32_t) * (size_t)B);
-    L->counter_bytes = L->cnt_draw +
-                       align256(sizeof(uint32_t) * (size_t)B * (size_t)(1 + (nt + kDrawGroup - 1) / kDrawGroup));
+    L->counter_bytes = align256(sizeof(uint32_t) * (size_t)B);
     size_t off = 0;
     L->seq = off;       off = align256(off + sizeof(SeqState) * (size_t)B);
     L->rows = off;      off = align256(off + sizeof(RowDesc) * (size_t)B * NR);
@@ -2580,11 +2599,14 @@ static hipError_t launch_sample_dt(const SampleArgs &a, hipStream_t st) {
     }
     const int64_t per_seq = (int64_t)(a.gamma + 1) * a.Ct + (int64_t)a.gamma * a.Cd;
     hipLaunchKernelGGL((stats_kernel<DTT, DTD, kStatsThreads, kStatsUnroll>), dim3((unsigned)(a.B * (1 + per_seq))),
-                       dim3(kStatsThreads), sizeof(RowDesc) * (size_t)NR, st, a);
+                       dim3(kStatsThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((draw_kernel<DTT, DTD, kSampThreads>), dim3((unsigned)(a.B * a.ntiles)), dim3(kSampThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((tile_kernel<DTT, DTD, kSampThreads>), dim3((unsigned)(a.B * a.ntiles)), dim3(kSampThreads),
+                       sizeof(RowDesc) * (size_t)NR, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((pick_kernel<DTT, DTD, kSampThreads>), dim3((unsigned)a.B), dim3(kSampThreads), 0, st, a);
     return hipGetLastError();
 }
 
