@@ -214,7 +214,7 @@ def main():
         def step(s):
             sv.spec_verify_sample(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
                                   w["temperature"], w["top_p"], d2t=s["d2t"], ws=ws, out=outs)
-        kernel = "topp_kernel" if w["top_p"] < 1 else "stats_kernel"
+        kernel = "topp_kernel" if w["top_p"] < 1 else "stats_kernel+tile_kernel+pick_kernel"
     elif w["kind"] == "greedy":
         B, g = w["tokens"].shape
         need = sv.sv_workspace_bytes_greedy(B, g, w["target"].shape[2])

@@ -70,7 +70,10 @@ constexpr int kCandCap = 2048;      // LDS slots for band tokens per row
 constexpr int kCandVecCap = 1024;   // LDS slots for band vectors (16 bytes each) per row
 constexpr int kKeptCap = 2048;      // kept-list entries stored per row
 constexpr int kQListCap = 1024;     // q lists up to this size are matched in LDS during a draw
-constexpr int kTile = 4096;         // most target ids per residual/bonus tile
+#ifndef SV_TILE
+#define SV_TILE 2048
+#endif
+constexpr int kTile = SV_TILE;      // most target ids per residual/bonus tile
 constexpr int kTileMin = 1024;      // fewest (tiles shrink for small batches)
 constexpr int kDrawMinWgs = 512;    // tiles shrink until the draw has this many workgroups
 #ifndef SV_STATS_MIN_WGS
