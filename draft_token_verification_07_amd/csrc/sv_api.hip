@@ -196,6 +196,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.kept_stride = kept_stride(Vt, Vd);
     a.probe = reinterpret_cast<Probe *>(data + L.probe);
     a.tile_mass = reinterpret_cast<uint64_t *>(data + L.tile_mass);
+    a.tile_sub = reinterpret_cast<uint64_t *>(data + L.tile_sub);
     a.tile_jb = reinterpret_cast<int32_t *>(data + L.tile_jb);
 
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -75,6 +75,7 @@ constexpr int kQListCap = 1024;     // q lists up to this size are matched in LD
 #endif
 constexpr int kTile = SV_TILE;      // most target ids per residual/bonus tile
 constexpr int kTileMin = 1024;      // fewest (tiles shrink for small batches)
+constexpr int kSubTiles = 64;       // equal id ranges per tile whose masses the pick reads
 constexpr int kDrawMinWgs = 512;    // tiles shrink until the draw has this many workgroups
 #ifndef SV_STATS_MIN_WGS
 #define SV_STATS_MIN_WGS 256
@@ -168,6 +169,7 @@ struct SampleArgs {
     int32_t kept_stride;       // min(kKeptCap, max(Vt, Vd))
     Probe *probe;              // [B, gamma] (plain mode)
     uint64_t *tile_mass;       // [B, ntiles] fixed-point draw masses (plain mode)
+    uint64_t *tile_sub;        // [B, ntiles, kSubTiles] the same by subtile (plain mode)
     int32_t *tile_jb;          // [ntiles + 1] first draft id of each draw tile under d2t (plain mode)
 };
 
@@ -191,7 +193,7 @@ inline bool workspace_fits(size_t W, size_t counter_bytes, size_t data_bytes) {
 
 struct WorkspaceLayout {
     size_t cnt_stats, counter_bytes;                         // offsets from 0
-    size_t seq, rows, part, kept, probe, tile_mass, tile_jb, data_bytes;   // offsets from K
+    size_t seq, rows, part, kept, probe, tile_mass, tile_sub, tile_jb, data_bytes;   // offsets from K
 };
 // Workspace layout and launch shape of one sampling call; bt / bd are the
 // element sizes of the target / draft logits.  4-byte elements give the

@@ -282,7 +282,7 @@ template <int G>
 __device__ __forceinline__ int32_t group_lower_bound(const int32_t *v, int32_t n, int32_t t) {
     const int lane = threadIdx.x & (kWave - 1);
     const int gl = lane & (G - 1);
-    const uint64_t gmask = (G == kWave ? ~0ull : ((1ull << G) - 1ull)) << (lane & ~(G - 1));
+    const uint64_t gmask = (G == kWave ? ~0ull : ((1ull << (G & (kWave - 1))) - 1ull)) << (lane & ~(G - 1));
     int32_t lo = 0, hi = n;                       // the group's answer lies in [lo, hi]
     while (__ballot(hi - lo > G)) {
         const bool active = hi - lo > G;
@@ -2121,10 +2121,10 @@ struct DrawTile {
     }
 };
 
+// Row pointers, modes and normalisers of a draw over target row n.
 template <int DTT, int DTD, int NT>
-__device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const SampleArgs &a, int32_t b,
-                                               int32_t n, const RowDesc &dp, const RowDesc &dq, int32_t k,
-                                               int32_t j0, int32_t j1, float *s_q) {
+__device__ __forceinline__ void draw_tile_params(DrawTile<DTT, DTD, NT> &x, const SampleArgs &a, int32_t b,
+                                                 int32_t n, const RowDesc &dp, const RowDesc &dq) {
     using ET = Elem<DTT>;
     using ED = Elem<DTD>;
     const int32_t g = a.gamma;
@@ -2143,6 +2143,15 @@ __device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const 
     x.nomass = (dp.flags & RD_NO_MASS) != 0;
     x.mq = dq.m;
     x.izq = (dq.flags & RD_NO_MASS) ? 0.0f : 1.0f / dq.Zk;
+}
+
+template <int DTT, int DTD, int NT>
+__device__ __forceinline__ void draw_tile_load(DrawTile<DTT, DTD, NT> &x, const SampleArgs &a, int32_t b,
+                                               int32_t n, const RowDesc &dp, const RowDesc &dq, int32_t k,
+                                               int32_t j0, int32_t j1, float *s_q) {
+    using ET = Elem<DTT>;
+    using ED = Elem<DTD>;
+    draw_tile_params<DTT, DTD, NT>(x, a, b, n, dp, dq);
     x.t0 = k * a.tile;
     x.t1 = min(a.Vt, x.t0 + a.tile);
     const int32_t body0 = x.sp.head, body1 = x.sp.head + x.sp.nvec * ET::kPerVec;
@@ -2209,19 +2218,21 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
     constexpr int NW = NT / kWave;
     static_assert(NT > SV_MAX_GAMMA, "one thread per draft position");
     extern __shared__ RowDesc s_rows[];                       // [2 * gamma + 1]
-    __shared__ MaxSum s_part[kPartCap];
+    constexpr int kTilePartCap = 256;                         // partials staged in LDS (else read twice)
+    __shared__ MaxSum s_part[kTilePartCap];
     __shared__ float s_q[kTile];
-    __shared__ uint64_t s_tmp[NW];
+    __shared__ uint64_t s_sub[kSubTiles];
 
     const int32_t g = a.gamma, NR = 2 * g + 1;
     const int32_t per_seq = (g + 1) * a.Ct + g * a.Cd;
     const int32_t b = blockIdx.x / a.ntiles, k = blockIdx.x % a.ntiles;
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    if ((int)threadIdx.x < kSubTiles) s_sub[threadIdx.x] = 0;
 
     // one round of loads: the chunk partials (into LDS), this thread's draft
     // position (token, probe, uniform), the tile's draft-id range
     const MaxSum *part = a.part + (size_t)b * per_seq;
-    const bool staged = per_seq <= kPartCap;
+    const bool staged = per_seq <= kTilePartCap;
     if (staged)
         for (int32_t q = threadIdx.x; q < per_seq; q += NT) s_part[q] = part[q];
     const int32_t i = threadIdx.x;
@@ -2317,19 +2328,38 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
     const RowDesc dq = n < g ? s_rows[g + 1 + n] : dp;
     DT x;
     draw_tile_load<DTT, DTD, NT>(x, a, b, n, dp, dq, k, j0, j1, s_q);
-    auto none = [](int32_t, uint64_t) {};
-    uint64_t sm = 0;
+    // masses by subtile (kSubTiles equal id ranges of the tile, in id order);
+    // a vector's ids fall in at most two subtiles
+    const int sh = __builtin_ctz((unsigned)(a.tile / kSubTiles));
+    int cur = -1;
+    uint64_t acc = 0;
+    auto flush = [&]() {
+        if (cur >= 0 && acc) atomicAdd(reinterpret_cast<unsigned long long *>(&s_sub[cur]), (unsigned long long)acc);
+    };
+    auto add = [&](int32_t tt, uint64_t w) {
+        const int sidx = (tt - x.t0) >> sh;
+        if (sidx != cur) {
+            flush();
+            cur = sidx;
+            acc = 0;
+        }
+        acc += w;
+    };
 #pragma unroll
-    for (int u = 0; u < U; ++u) sm += x.slice(u, s_q, none);
+    for (int u = 0; u < U; ++u) (void)x.slice(u, s_q, add);
+    flush();
     const int32_t te = x.edge_id();
-    if (te >= 0) sm += x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q));
-    sm = wave_total_u64(sm);
-    if (lane == 0) s_tmp[wv] = sm;
+    if (te >= 0) {
+        const uint64_t w = x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q));
+        if (w) atomicAdd(reinterpret_cast<unsigned long long *>(&s_sub[(te - x.t0) >> sh]), (unsigned long long)w);
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t mass = 0;
-        for (int w = 0; w < NW; ++w) mass += s_tmp[w];
-        a.tile_mass[(size_t)b * a.ntiles + k] = mass;
+    if (wv == 0) {
+        static_assert(kSubTiles == kWave, "one subtile per lane of the first wave");
+        const uint64_t v = s_sub[lane];
+        a.tile_sub[((size_t)b * a.ntiles + k) * kSubTiles + lane] = v;
+        const uint64_t mass = wave_total_u64(v);
+        if (lane == 0) a.tile_mass[(size_t)b * a.ntiles + k] = mass;
     }
 }
 
@@ -2341,10 +2371,11 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
     using DT = DrawTile<DTT, DTD, NT>;
     constexpr int U = DT::U;
     constexpr int NW = NT / kWave;
-    __shared__ float s_q[kTile];
+    __shared__ float s_q[kTile];                  // rare fallback (zero residual mass)
     __shared__ uint64_t s_tmp[NW];
-    __shared__ uint64_t s_blk[(U + 2) * NW];      // search: per (slice, wave) totals, edge ids
-    __shared__ uint64_t s_pick[2];
+    __shared__ int32_t s_qj[kWave];               // draft id of each target id of the subtile (d2t)
+    __shared__ uint64_t s_pick[2];                // picked tile, offset of floor(u * S) inside it
+    __shared__ uint64_t s_sp[2];                  // picked subtile, offset inside it
     __shared__ int32_t s_jr[2];
     __shared__ int32_t s_tok;
     // rare fallback (zero residual mass)
@@ -2359,7 +2390,9 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
     const int32_t n = st->n;
     const RowDesc dp = load_desc(&st->dp), dq = load_desc(&st->dq);
     const uint64_t *mass = a.tile_mass + (size_t)b * a.ntiles;
+    static_assert(kTile / kSubTiles <= kWave, "a subtile fits one wave");
     DT x;
+    draw_tile_params<DTT, DTD, NT>(x, a, b, n, dp, dq);
     const float u_s = a.u_s[b];
     // S and the tile holding floor(u * S): one round of loads when the tiles
     // fit one per thread (else a first sweep for S, a second for the pick)
@@ -2419,94 +2452,59 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
             const int32_t kp = (int32_t)s_pick[0];
             const uint64_t tin = s_pick[1];
             const int32_t pj0 = a.d2t ? s_jr[0] : 0, pj1 = a.d2t ? s_jr[1] : 0;
-            __syncthreads();
-            draw_tile_load<DTT, DTD, NT>(x, a, b, n, dp, dq, kp, pj0, pj1, s_q);
-            // order of the tile's ids: the head ids, the slices (thread order
-            // inside each), the tail ids.  Each wave puts its slice totals in
-            // LDS; every thread then finds the block holding tin by itself.
-            auto none = [](int32_t, uint64_t) {};
-            uint64_t su[U];
+            // one round of loads: the tile's subtile masses and, with d2t, the
+            // target ids of its draft ids
+            const int32_t sw = a.tile / kSubTiles, t0 = kp * a.tile;
+            uint64_t sm = 0;
+            if (wv == 0) sm = a.tile_sub[((size_t)b * a.ntiles + kp) * kSubTiles + lane];
+            constexpr int UJ = kTile / NT;
+            int32_t tj[UJ];
+            const bool mapped = x.mapped && pj1 > pj0;
+            if (mapped) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) su[u] = x.slice(u, s_q, none);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint64_t t = wave_total_u64(su[u]);
-                if (lane == 0) s_blk[u * NW + wv] = t;
+                for (int u = 0; u < UJ; ++u) tj[u] = a.d2t[min(pj0 + u * NT + (int32_t)threadIdx.x, pj1 - 1)];
             }
-            // head / tail ids (at most 7 of each) exist in the first and last tiles only
-            const int32_t body1 = x.sp.head + x.sp.nvec * Elem<DTT>::kPerVec;
-            const bool edges = x.t0 < x.sp.head || x.t1 > body1;
-            if (threadIdx.x < 2) s_blk[U * NW + threadIdx.x] = 0;
+            if ((int32_t)threadIdx.x < sw) s_qj[threadIdx.x] = -1;
+            if (threadIdx.x == 0) {
+                s_sp[0] = 0;
+                s_sp[1] = ~0ull;                          // no token unless a subtile brackets tin
+            }
+            if (wv == 0) {
+                // the subtile holding tin (exact sums, so the bracket is unique)
+                const uint64_t inc = wave_incl_scan_u64_dpp(sm);
+                if (sm > 0 && inc - sm <= tin && tin < inc) {
+                    s_sp[0] = (uint64_t)lane;
+                    s_sp[1] = tin - (inc - sm);
+                }
+            }
+            __syncthreads();
+            const int32_t ts = t0 + (int32_t)s_sp[0] * sw;
+            const uint64_t tin2 = s_sp[1];
+            if (mapped) {
+#pragma unroll
+                for (int u = 0; u < UJ; ++u) {
+                    const int32_t j = pj0 + u * NT + (int32_t)threadIdx.x;
+                    const int32_t ii = tj[u] - ts;
+                    if (j < pj1 && ii >= 0 && ii < sw) s_qj[ii] = j;
+                }
+            }
             if (threadIdx.x == 0) s_tok = -1;
-            if (edges) {
-                __syncthreads();
-                const int32_t te = x.edge_id();
-                if (te >= 0)
-                    atomicAdd(reinterpret_cast<unsigned long long *>(&s_blk[U * NW + (te < x.sp.head ? 0 : 1)]),
-                              (unsigned long long)x.weight_q(Elem<DTT>::load(x.trow, te), x.q_single(te, s_q)));
-            }
             __syncthreads();
-            // blocks in id order: head, (u, w) for u, w ascending, tail
-            int blk = -3;                               // the tail unless found earlier
-            uint64_t off;
-            {
-                uint64_t r = s_blk[U * NW];
-                if (tin < r) {
-                    blk = -2;
-                    off = tin;
-                } else {
-                    off = tin - r;
-                    for (int i = 0; i < U * NW; ++i) {
-                        const uint64_t m = s_blk[i];
-                        if (blk == -3 && m > 0 && tin < r + m) {
-                            blk = i;
-                            off = tin - r;
-                        }
-                        r += m;
-                    }
-                    if (blk == -3) off = tin - r;
+            if (wv == 0) {
+                // one wave weighs the subtile's ids in order, as the tile pass did
+                const int32_t t = ts + lane;
+                const bool v = lane < sw && t < a.Vt;
+                const float zt = Elem<DTT>::load(x.trow, min(t, a.Vt - 1));
+                float q = 0.0f;
+                if (x.resid) {
+                    const int32_t j = x.mapped ? (lane < sw ? s_qj[lane] : -1) : min(t, a.Vd - 1);
+                    const float zq = Elem<DTD>::load(x.drow, max(j, 0));
+                    if (j >= 0) q = x.qprob(zq);
                 }
-            }
-            if (blk >= 0) {
-                // wave blk % NW, slice blk / NW: the lane whose prefix brackets off
-                const int bu = blk / NW, bw = blk % NW;
-                if (wv == bw) {
-                    uint64_t mine = 0;
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        if (u == bu) mine = su[u];
-                    const uint64_t inc = wave_incl_scan_u64_dpp(mine);
-                    const uint64_t exc = inc - mine;
-                    if (mine > 0 && exc <= off && off < inc) {
-                        uint64_t rr = exc;
-                        int32_t found = -1;
-                        auto walk = [&](int32_t t, uint64_t w) {
-                            if (found < 0 && w > 0) {
-                                rr += w;
-                                if (rr > off) found = t;
-                            }
-                        };
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            if (u == bu) (void)x.slice(u, s_q, walk);
-                        s_tok = found;
-                    }
-                }
-            } else if (threadIdx.x == 0) {
-                // head (blk == -2) or tail (blk == -3) ids, walked in order
-                const int32_t lo = blk == -2 ? max(x.t0, 0) : max(x.t0, body1);
-                const int32_t hi = blk == -2 ? min(x.t1, x.sp.head) : x.t1;
-                uint64_t rr = 0;
-                int32_t found = -1, lastpos = -1;
-                for (int32_t t = lo; t < hi && found < 0; ++t) {
-                    const uint64_t w = x.weight_q(Elem<DTT>::load(x.trow, t), x.q_single(t, s_q));
-                    if (w > 0) {
-                        lastpos = t;
-                        rr += w;
-                        if (rr > off) found = t;
-                    }
-                }
-                s_tok = found >= 0 ? found : lastpos;
+                const uint64_t w = v ? x.weight_q(zt, q) : 0ull;
+                const uint64_t inc = wave_incl_scan_u64_dpp(w);
+                const uint64_t hb = __ballot(w > 0 && inc > tin2 && inc - w <= tin2);
+                if (lane == 0 && hb) s_tok = ts + __ffsll((unsigned long long)hb) - 1;
             }
             __syncthreads();
             tok = s_tok;
@@ -2580,6 +2578,7 @@ bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt,
     L->kept = off;      off = align256(off + (topp ? sizeof(KeptEnt) * (size_t)B * NR * kept_stride(Vt, Vd) : 0));
     L->probe = off;     off = align256(off + (topp ? 0 : sizeof(Probe) * (size_t)B * (size_t)gamma));
     L->tile_mass = off; off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt));
+    L->tile_sub = off;  off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt * kSubTiles));
     L->tile_jb = off;   off = align256(off + (topp ? 0 : sizeof(int32_t) * ((size_t)nt + 1)));
     L->data_bytes = off;
     *Ct = ct;
