@@ -2252,24 +2252,49 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
         j1 = min(max(a.tile_jb[k + 1], j0), a.Vd);
     }
     __syncthreads();
-    // row r is merged by thread r, chunk by chunk in order (identical rows
-    // give identical results)
-    for (int32_t r = threadIdx.x; r < NR; r += NT) {
-        const bool tgt = r <= g;
-        const int32_t C = tgt ? a.Ct : a.Cd;
-        const int32_t off = tgt ? r * a.Ct : (g + 1) * a.Ct + (r - g - 1) * a.Cd;
-        MaxSum acc = staged ? s_part[off] : part[off];
-        for (int32_t q = 1; q < C; ++q) acc = maxsum_merge(acc, staged ? s_part[off + q] : part[off + q], a.c);
+    // Rows of few chunks are merged by one thread each, chunk by chunk in
+    // order; rows of many by one wave each (lane l folds chunks l, l + 64, ...
+    // in order, then the lanes combine by DPP).  Either way the pattern is fixed
+    // by the row's chunk count, so identical rows give identical results.
+    auto put_row = [&](int32_t r, const MaxSum &acc) {
         RowDesc d;
         d.m = acc.m;
         d.Z = acc.s;
         d.Zk = acc.s;
         d.key = 0u;
         d.tie_cut = INT32_MAX;
-        d.nkept = tgt ? a.Vt : a.Vd;
+        d.nkept = r <= g ? a.Vt : a.Vd;
         d.flags = bad_max(acc.m) ? RD_NO_MASS : 0;
         d.ptok = 0.0f;
         s_rows[r] = d;
+    };
+    constexpr int32_t kSerialChunks = 8;
+    auto row_chunks = [&](int32_t r, int32_t &C, int32_t &off) {
+        const bool tgt = r <= g;
+        C = tgt ? a.Ct : a.Cd;
+        off = tgt ? r * a.Ct : (g + 1) * a.Ct + (r - g - 1) * a.Cd;
+    };
+    for (int32_t r = threadIdx.x; r < NR; r += NT) {
+        int32_t C, off;
+        row_chunks(r, C, off);
+        if (C > kSerialChunks) continue;
+        MaxSum acc = staged ? s_part[off] : part[off];
+        for (int32_t q = 1; q < C; ++q) acc = maxsum_merge(acc, staged ? s_part[off + q] : part[off + q], a.c);
+        put_row(r, acc);
+    }
+    if (a.Ct > kSerialChunks || a.Cd > kSerialChunks) {
+        for (int32_t r = wv; r < NR; r += NW) {
+            int32_t C, off;
+            row_chunks(r, C, off);
+            if (C <= kSerialChunks) continue;                // wave-uniform
+            MaxSum acc;
+            acc.m = -INFINITY;
+            acc.s = 0.0f;
+            for (int32_t q = lane; q < C; q += kWave)
+                acc = maxsum_merge(acc, staged ? s_part[off + q] : part[off + q], a.c);
+            acc = wave_maxsum_dpp(acc, a.c);
+            if (lane == 0) put_row(r, acc);
+        }
     }
     __syncthreads();
     // the chain: n is the first position where u * q < p fails (exactly:
