@@ -22,12 +22,8 @@ bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
 // greedy / tree: counters [B] (+ [B, R] when rows are chunked) below K;
 // (value, index) row results [B, R] and chunk partials [B, R, C] above
 int32_t greedy_C(int32_t B, int32_t R, int32_t V) { return greedy_chunks(V, (int64_t)B * R); }
-size_t greedy_group_offset(int32_t B, int32_t R, int32_t V) {
-    return (size_t)B * (greedy_C(B, R, V) > 1 ? 1 + (size_t)R : 1);
-}
 size_t greedy_counter_bytes(int32_t B, int32_t R, int32_t V) {
-    const size_t ng = (size_t)(R + kRowGroup - 1) / kRowGroup;
-    return align256(sizeof(uint32_t) * (greedy_group_offset(B, R, V) + (ng > 1 ? (size_t)B * ng : 0)));
+    return align256(sizeof(uint32_t) * (size_t)B * (greedy_C(B, R, V) > 1 ? 1 + (size_t)R : 1));
 }
 size_t greedy_rowres_bytes(int32_t B, int32_t R) { return align256(sizeof(ArgMax) * (size_t)B * R); }
 size_t greedy_data_bytes(int32_t B, int32_t R, int32_t V) {
@@ -58,7 +54,6 @@ sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, con
     char *base = static_cast<char *>(ws);
     char *data = base + counter_region(ws_bytes);
     a.counters = reinterpret_cast<uint32_t *>(base);
-    a.group_counters = (int64_t)greedy_group_offset(B, R, V);
     a.rowres = reinterpret_cast<ArgMax *>(data);
     a.part = reinterpret_cast<ArgMax *>(data + greedy_rowres_bytes(B, R));
     if (!grid_fits((int64_t)B * R * a.chunks)) return SV_ERR_TOO_LARGE;

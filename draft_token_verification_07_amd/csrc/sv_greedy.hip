@@ -20,11 +20,16 @@
 
 namespace sv {
 
-template <int DT, int NT, int U>
+template <int NT>
+__device__ __forceinline__ void greedy_sequence(const GreedyArgs &a, int32_t b, int32_t *gmax);
+
+// SPLIT: sequences of more than kRowGroup rows end the launch after the row
+// results; seq_kernel runs their combine and walk (a kernel boundary costs
+// less than two arrival levels).
+template <int DT, int NT, int U, bool SPLIT>
 __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     __shared__ ArgMax red[NT / kWave];
     __shared__ int last_flag;
-    __shared__ int32_t s_n, s_status;
     // epilogue scratch, sized by the launch: gmax[R], tok[R] int32, then
     // (tree) par[R] int32, depth[R] int16, acc[R] uint8
     extern __shared__ int32_t gmax[];
@@ -117,22 +122,25 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
             r0 = argmax_merge(r0, k < kMaxChunksMerged ? s_ch[k] : sub(&a.part[(size_t)row * C + k]));
     }
     if (threadIdx.x == 0) pub(&a.rowres[row], r0);
+    if constexpr (SPLIT) return;
 
     // ---- last workgroup of the sequence: combine and walk ----------------
-    // Rows of a sequence finish together; with many rows, a first arrival
-    // level per group of kRowGroup rows keeps the atomics on one counter few.
-    {
-        const int32_t ng = (R + kRowGroup - 1) / kRowGroup;
-        if (ng > 1) {
-            const int32_t grp = (row % R) / kRowGroup;
-            const uint32_t gsz = (uint32_t)min(kRowGroup, R - grp * kRowGroup);
-            if (!arrive_last(&a.counters[a.group_counters + (size_t)b * ng + grp], gsz, &last_flag)) return;
-            if (!arrive_last(&a.counters[b], (uint32_t)ng, &last_flag)) return;
-        } else if (!arrive_last(&a.counters[b], (uint32_t)R, &last_flag)) {
-            return;
-        }
-    }
+    if (!arrive_last(&a.counters[b], (uint32_t)R, &last_flag)) return;
+    greedy_sequence<NT>(a, b, gmax);
+}
 
+// One workgroup per sequence, after greedy_kernel<..., true>.
+template <int NT>
+__global__ __launch_bounds__(NT) void seq_kernel(GreedyArgs a) {
+    extern __shared__ int32_t gmax[];
+    greedy_sequence<NT>(a, blockIdx.x, gmax);
+}
+
+// Combine the row results of sequence b and run the chain or the tree walk.
+template <int NT>
+__device__ __forceinline__ void greedy_sequence(const GreedyArgs &a, int32_t b, int32_t *gmax) {
+    __shared__ int32_t s_n, s_status;
+    const int32_t R = a.rows_per_seq;
     // one round of loads: the row results, the draft tokens (and parents)
     static_assert(NT >= kWave, "one wave at least");
     const int32_t nt = a.tree ? R : R - 1;               // tokens per sequence
@@ -243,8 +251,16 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
     const size_t R = (size_t)a.rows_per_seq;
     // gmax[R], tok[R], then (tree) par[R], depth[R] int16, acc[R] uint8
     const size_t lds = 2 * R * sizeof(int32_t) + (a.tree ? R * (sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
-    hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll>), dim3(grid),
-                       dim3(kGreedyThreads), lds, st, a);
+    if (a.rows_per_seq <= kRowGroup) {
+        hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, false>), dim3(grid),
+                           dim3(kGreedyThreads), lds, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, true>), dim3(grid), dim3(kGreedyThreads), 0,
+                       st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seq_kernel<kGreedyThreads>), dim3(a.B), dim3(kGreedyThreads), lds, st, a);
     return hipGetLastError();
 }
 

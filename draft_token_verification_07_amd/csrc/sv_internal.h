@@ -50,7 +50,7 @@ constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
 constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
 constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
 constexpr int kMaxChunksMerged = 256;               // chunk results a row merge stages in LDS
-constexpr int kRowGroup = 8;                        // rows per first-level arrival counter
+constexpr int kRowGroup = 8;                        // longer sequences end the row launch and walk in a second
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
 constexpr int kStatsUnroll = SV_STATS_UNROLL;
 constexpr int kStatsItersPerWg = SV_STATS_ITERS;
@@ -100,9 +100,7 @@ struct GreedyArgs {
     int32_t *out_tokens, *out_len, *out_status, *out_path;
     ArgMax *part;              // [B * rows_per_seq * chunks] chunk results (chunks > 1)
     ArgMax *rowres;            // [B * rows_per_seq] row results
-    uint32_t *counters;        // [B] sequences, [B * rows_per_seq] rows (chunks > 1),
-                               // then from group_counters [B * ceil(rows_per_seq / kRowGroup)]
-    int64_t group_counters;    // offset of the row-group counters in counters
+    uint32_t *counters;        // [B] sequences, then [B * rows_per_seq] rows (chunks > 1)
 };
 
 int32_t greedy_chunks(int32_t V, int64_t rows);
