@@ -740,7 +740,8 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 // sum is independent of the order of its terms.
 constexpr double kFixW = 2147483648.0;          // 2^31
 __device__ __forceinline__ uint32_t fixw32(float z, float m, float c) {
-    return (uint32_t)((double)exp2_hw((z - m) * c) * kFixW);
+    // w * 2^31 is exact in float32 (w <= 1), and the conversion truncates
+    return (uint32_t)(exp2_hw((z - m) * c) * 2147483648.0f);
 }
 
 // Ordering code of a band token: (key << 32) | ~id.  Token j is ahead of
@@ -884,7 +885,7 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
 // fixed-point mass and count give, by a scan that every wave runs alike, the
 // bin holding the boundary; only that bin's tokens are ranked against each
 // other.  The kept set is every band token whose ordering code is at least
-// the boundary's -- the set the general path finds.  Four workgroup barriers.
+// the boundary's -- the set the general path finds.  Five workgroup barriers.
 // Returns false, having written nothing to global memory and left the band
 // vectors in LDS, when the row needs the general path.
 constexpr int kBinMembers = 224;        // tokens of the boundary bin ranked here
@@ -915,20 +916,12 @@ __device__ __forceinline__ bool bin_select(const void *row, const RowSplit &sp, 
     const float thr = m - band;
     const float bscale = (float)NB / band;
     auto bin_of = [&](float z) { return (int)fminf((m - z) * bscale, (float)(NB - 1)); };
-    // -0 is folded onto +0 so that the ordering code orders values
+    // A. band tokens as (logit bits, id): one band vector per thread, its
+    // tokens in consecutive slots; -0 is folded onto +0 so that the ordering
+    // code below orders values
     auto put = [&](int32_t pos, float z, int32_t id) {
-        if (pos < kCandCap) {
-            const float zf = z + 0.0f;
-            const uint32_t fw = fixw32(zf, m, c);
-            l.P[pos] = pcode(fkey(zf), id);
-            l.fw[pos] = fw;
-            const int bn = bin_of(zf);
-            atomicAdd(reinterpret_cast<unsigned long long *>(&l.bm[bn]), (unsigned long long)fw);
-            atomicAdd(&l.bc[bn], 1u);
-        }
+        if (pos < kCandCap) l.P[pos] = ((uint64_t)__float_as_uint(z + 0.0f) << 32) | (uint32_t)id;
     };
-
-    // A. band tokens: one band vector per thread, its tokens in consecutive slots
     for (int32_t t0 = 0; t0 < nvc; t0 += NT) {
         const int32_t t = t0 + (int32_t)threadIdx.x;
         float x[E::kPerVec];
@@ -960,12 +953,24 @@ __device__ __forceinline__ bool bin_select(const void *row, const RowSplit &sp, 
         if (in) put(pos, z, j);
     }
     __syncthreads();
+    // ordering codes, fixed-point weights and bin totals, one token per thread
+    const int32_t n = l.cnt[0];
+    if (n > kCandCap) return false;
+    for (int32_t t = threadIdx.x; t < n; t += NT) {
+        const uint64_t r = l.P[t];
+        const float z = __uint_as_float((uint32_t)(r >> 32));
+        const uint32_t fw = fixw32(z, m, c);
+        l.P[t] = pcode(fkey(z), (int32_t)(uint32_t)r);
+        l.fw[t] = fw;
+        const int bn = bin_of(z);
+        atomicAdd(reinterpret_cast<unsigned long long *>(&l.bm[bn]), (unsigned long long)fw);
+        atomicAdd(&l.bc[bn], 1u);
+    }
+    __syncthreads();
 
     // B. the boundary bin, in every wave alike: the first bin whose inclusive
     // mass exceeds T0 (the band must hold more than T0, with the margin of the
     // general path); then its tokens, compacted
-    const int32_t n = l.cnt[0];
-    if (n > kCandCap) return false;
     const uint64_t bm = l.bm[lane];
     const int32_t bc = (int32_t)l.bc[lane];
     const uint64_t binc = wave_incl_scan_u64_dpp(bm);
@@ -1640,12 +1645,15 @@ __device__ __forceinline__ int32_t group_draw_list(const SampleArgs &a, const Ro
     }
     // q of entry i: at most one of q's entries has its id (ids are distinct)
     float qpart = 0.0f;
-    if (has)
-        for (int32_t j = sl; j < Kq; j += G) {
+#pragma unroll
+    for (int it = 0; it < kWave / G; ++it) {
+        const int32_t j = sl + it * G;
+        if (has && j < Kq) {
             const KeptEnt qe = pq[j];
             const int32_t qid = a.d2t ? s_qid[j] : qe.id;
             if (qid == e.id) qpart = qe.w / dq.Zk;
         }
+    }
     const float q = half_row_sum_f32(qpart);
     for (int attempt = 0; attempt < 2; ++attempt) {
         const bool use_resid = resid && attempt == 0;
@@ -1659,10 +1667,14 @@ __device__ __forceinline__ int32_t group_draw_list(const SampleArgs &a, const Ro
         __syncthreads();
         // mass of the entries with id <= this entry's, and the total
         uint64_t inc = 0, S = 0;
-        for (int32_t j = sl; j < K; j += G) {
-            const uint64_t rj = s_rf[j];
-            S += rj;
-            if (s_id[j] <= e.id) inc += rj;
+#pragma unroll
+        for (int it = 0; it < kWave / G; ++it) {
+            const int32_t j = sl + it * G;
+            if (j < K) {
+                const uint64_t rj = s_rf[j];
+                S += rj;
+                if (s_id[j] <= e.id) inc += rj;
+            }
         }
         inc = half_row_sum_u64(inc);
         S = half_row_sum_u64(S);
