@@ -1163,12 +1163,17 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         __syncthreads();
         tile(raw, xv, vm, tm, threadIdx.x, nu);
     }
+    // Waves with more of their row left issue first, so that rows sharing a
+    // CU finish together instead of oldest-first: level floor(4 (full - it) /
+    // (full + 1)), i.e. the number of k in 1..3 with it <= lim_k (no division
+    // in the loop).
     int prio = -1;
+    const int32_t lim1 = full - (1 * (full + 1) + 3) / 4;
+    const int32_t lim2 = full - (2 * (full + 1) + 3) / 4;
+    const int32_t lim3 = full - (3 * (full + 1) + 3) / 4;
     for (int32_t it = 1; it < full; ++it) {
         {
-            // waves with more of their row left issue first, so that rows
-            // sharing a CU finish together instead of oldest-first
-            const int lvl = (int)(((int64_t)(full - it) * 4) / (full + 1));
+            const int lvl = (it <= lim1) + (it <= lim2) + (it <= lim3);
             if (lvl != prio) {
                 prio = lvl;
                 if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
