@@ -206,6 +206,51 @@ def test_sample_topp_ties_at_cutoff(oracle_mod):
     _check_sample(oracle_mod, w, "top-p ties")
 
 
+@pytest.mark.parametrize("per_value,fp32", [(40, False), (120, True), (300, False)])
+def test_sample_topp_tie_groups_in_band(oracle_mod, per_value, fp32):
+    """A band of a few hundred tokens made of tie groups (equal logits): the
+    cutoff falls inside a group, which the bin select ranks by id.  With 300
+    tokens on one value the boundary bin is too crowded for it, and the row
+    takes the sub-band path instead."""
+    rng = np.random.default_rng(45 + per_value)
+    B, g, V = 6, 3, 4001
+    vals = np.array([5.0, 4.5, 4.0, 3.5, 3.0], np.float32)
+    zt = np.full((B, g + 1, V), -40.0, np.float32)
+    for b in range(B):
+        for r in range(g + 1):
+            ids = rng.choice(V, per_value * len(vals), replace=False)
+            zt[b, r, ids] = np.repeat(vals, per_value)
+    zd = zt[:, :g].copy()
+    flip = rng.random((B, g, V)) < 0.1
+    zd[flip] = vals[rng.integers(0, len(vals), flip.sum())]
+    tok = np.argmax(zd, axis=2).astype(np.int32)
+    cv = (lambda x: x) if fp32 else synth.bf16_bits
+    w = dict(target=cv(zt), draft=cv(zd), tokens=tok, u_accept=synth.uniforms(rng, (B, g)),
+             u_sample=synth.uniforms(rng, (B,)), d2t=None, temperature=1.0, top_p=0.7)
+    _check_sample(oracle_mod, w, "top-p tie groups %d" % per_value)
+
+
+def test_sample_tiny_top_p_is_greedy(oracle_mod):
+    """top_p -> 0 keeps only the lowest-id argmax of p and of q; with draft
+    tokens equal to the draft argmax, sampling verification reduces to
+    greedy verification (the same tokens and accepted lengths)."""
+    import torch
+    import draft_token_verification_07_amd as sv
+    from helpers import to_dev
+    rng = np.random.default_rng(46)
+    B, g, V = 8, 4, 30011
+    zt = (rng.standard_normal((B, g + 1, V)) * 2.0).astype(np.float32)
+    zd = zt[:, :g] + (rng.standard_normal((B, g, V)) * 0.7).astype(np.float32)
+    zt, zd = synth.bf16_bits(zt), synth.bf16_bits(zd)
+    tok = np.argmax(synth.bf16_to_f32(zd), axis=2).astype(np.int32)
+    out = sv.spec_verify_sample(to_dev(zt), to_dev(zd), to_dev(tok), to_dev(synth.uniforms(rng, (B, g))),
+                                to_dev(synth.uniforms(rng, (B,))), 0.9, 1e-9)
+    gr = sv.spec_verify_greedy(to_dev(zt), to_dev(tok))
+    torch.cuda.synchronize()
+    assert np.array_equal(out[0].cpu().numpy(), gr[0].cpu().numpy())
+    assert np.array_equal(out[1].cpu().numpy(), gr[1].cpu().numpy())
+
+
 @pytest.mark.parametrize("B,gamma,Vt,Vd,top_p", [(6, 3, 60013, 9001, 1.0), (4, 2, 20011, 5003, 0.9),
                                                  (3, 0, 9001, 1001, 1.0)])
 def test_sample_d2t_small(oracle_mod, B, gamma, Vt, Vd, top_p):
