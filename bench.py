@@ -232,7 +232,7 @@ def main():
 
         def step(s):
             sv.spec_verify_tree_greedy(s["target"], s["tokens"], s["parents"], ws=ws, out=outs)
-        kernel = "greedy_kernel"
+        kernel = "greedy_kernel+seq_kernel"
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     del bnd
 
