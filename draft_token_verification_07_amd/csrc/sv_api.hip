@@ -23,7 +23,8 @@ bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
 // (value, index) row results [B, R] and chunk partials [B, R, C] above
 int32_t greedy_C(int32_t B, int32_t R, int32_t V) { return greedy_chunks(V, (int64_t)B * R); }
 size_t greedy_counter_bytes(int32_t B, int32_t R, int32_t V) {
-    return align256(sizeof(uint32_t) * (size_t)B * (greedy_C(B, R, V) > 1 ? 1 + (size_t)R : 1));
+    const int32_t C = greedy_C(B, R, V);
+    return align256(sizeof(uint32_t) * (size_t)B * (C > 1 && !greedy_split(R, C) ? 1 + (size_t)R : 1));
 }
 size_t greedy_rowres_bytes(int32_t B, int32_t R) { return align256(sizeof(ArgMax) * (size_t)B * R); }
 size_t greedy_data_bytes(int32_t B, int32_t R, int32_t V) {
@@ -45,6 +46,7 @@ sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, con
     a.V = V;
     a.chunks = greedy_C(B, R, V);
     a.tree = tree ? 1 : 0;
+    a.split_chunks = greedy_split(R, a.chunks) && a.chunks > 1 ? 1 : 0;
     a.out_tokens = out_tokens;
     a.out_len = out_len;
     a.out_status = out_status;

@@ -23,9 +23,10 @@ namespace sv {
 template <int NT>
 __device__ __forceinline__ void greedy_sequence(const GreedyArgs &a, int32_t b, int32_t *gmax);
 
-// SPLIT: sequences of more than kRowGroup rows end the launch after the row
-// results; seq_kernel runs their combine and walk (a kernel boundary costs
-// less than two arrival levels).
+// SPLIT: the launch ends after the row (or chunk) results; seq_kernel merges
+// the chunks of each row and runs the combine and walk.  Taken for sequences
+// of more than kRowGroup rows and for rows cut in chunks (a kernel boundary
+// costs less than the arrival levels it replaces).
 template <int DT, int NT, int U, bool SPLIT>
 __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     __shared__ ArgMax red[NT / kWave];
@@ -105,24 +106,16 @@ __global__ __launch_bounds__(NT) void greedy_kernel(GreedyArgs a) {
     ArgMax r0 = red[0];
     for (int w = 1; w < NT / kWave; ++w) r0 = argmax_merge(r0, red[w]);
 
-    // ---- rows cut in several chunks: the last chunk of a row merges them ---
-    // (two arrival levels, so that no counter takes every chunk of a
-    // sequence at once)
-    if (C > 1) {
-        if (threadIdx.x == 0) pub(&a.part[(size_t)row * C + c], r0);
-        if (!arrive_last(&a.counters[a.B + row], (uint32_t)C, &last_flag)) return;
-        __shared__ ArgMax s_ch[kMaxChunksMerged];
-        for (int32_t k = threadIdx.x; k < C; k += NT) {
-            const ArgMax m = sub(&a.part[(size_t)row * C + k]);
-            if (k < kMaxChunksMerged) s_ch[k] = m;
+    if constexpr (SPLIT) {
+        // the sequence launch merges the chunks of each row
+        if (threadIdx.x == 0) {
+            if (C > 1) pub(&a.part[(size_t)row * C + c], r0);
+            else pub(&a.rowres[row], r0);
         }
-        __syncthreads();
-        r0 = s_ch[0];
-        for (int32_t k = 1; k < C; ++k)                                  // chunk order
-            r0 = argmax_merge(r0, k < kMaxChunksMerged ? s_ch[k] : sub(&a.part[(size_t)row * C + k]));
+        return;
     }
+    // (not split: the rows are whole, C == 1)
     if (threadIdx.x == 0) pub(&a.rowres[row], r0);
-    if constexpr (SPLIT) return;
 
     // ---- last workgroup of the sequence: combine and walk ----------------
     if (!arrive_last(&a.counters[b], (uint32_t)R, &last_flag)) return;
@@ -148,7 +141,15 @@ __device__ __forceinline__ void greedy_sequence(const GreedyArgs &a, int32_t b, 
     int32_t *tok = gmax + R;                              // [R] (tree and chain)
     int32_t *par = tok + R;                               // [R] (tree)
     for (int32_t r = threadIdx.x; r < R; r += NT) {
-        const ArgMax m = sub(&a.rowres[(size_t)b * R + r]);
+        ArgMax m;
+        if (a.split_chunks) {
+            // the row's chunk results, merged in chunk order
+            const ArgMax *pr = a.part + ((size_t)b * R + r) * a.chunks;
+            m = sub(&pr[0]);
+            for (int32_t k = 1; k < a.chunks; ++k) m = argmax_merge(m, sub(&pr[k]));
+        } else {
+            m = sub(&a.rowres[(size_t)b * R + r]);
+        }
         const int32_t t = r < nt ? a.tokens[(size_t)b * nt + r] : 0;
         const int32_t p = a.tree ? a.parents[(size_t)b * R + r] : 0;
         // a row of -inf everywhere: the lowest id attaining the maximum is 0
@@ -251,7 +252,7 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
     const size_t R = (size_t)a.rows_per_seq;
     // gmax[R], tok[R], then (tree) par[R], depth[R] int16, acc[R] uint8
     const size_t lds = 2 * R * sizeof(int32_t) + (a.tree ? R * (sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
-    if (a.rows_per_seq <= kRowGroup) {
+    if (!greedy_split(a.rows_per_seq, a.chunks)) {
         hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, false>), dim3(grid),
                            dim3(kGreedyThreads), lds, st, a);
         return hipGetLastError();
@@ -263,6 +264,8 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
     hipLaunchKernelGGL((seq_kernel<kGreedyThreads>), dim3(a.B), dim3(kGreedyThreads), lds, st, a);
     return hipGetLastError();
 }
+
+bool greedy_split(int32_t R, int32_t C) { return R > kRowGroup || C > 1; }
 
 // Chunks per row.  Counted in 8-element vectors whatever the dtype, so the
 // workspace size depends on V and the row count only (a float32 chunk is

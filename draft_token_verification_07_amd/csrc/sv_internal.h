@@ -49,7 +49,6 @@ constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
 constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
 constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
 constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
-constexpr int kMaxChunksMerged = 256;               // chunk results a row merge stages in LDS
 constexpr int kRowGroup = 8;                        // longer sequences end the row launch and walk in a second
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
 constexpr int kStatsUnroll = SV_STATS_UNROLL;
@@ -97,13 +96,15 @@ struct GreedyArgs {
     const int32_t *parents;    // tree only: [B, N]
     int32_t B, rows_per_seq, V, chunks;
     int32_t tree;
+    int32_t split_chunks;      // the sequence launch merges chunk results (split launch, chunks > 1)
     int32_t *out_tokens, *out_len, *out_status, *out_path;
     ArgMax *part;              // [B * rows_per_seq * chunks] chunk results (chunks > 1)
     ArgMax *rowres;            // [B * rows_per_seq] row results
-    uint32_t *counters;        // [B] sequences, then [B * rows_per_seq] rows (chunks > 1)
+    uint32_t *counters;        // [B] sequences (single-launch path)
 };
 
 int32_t greedy_chunks(int32_t V, int64_t rows);
+bool greedy_split(int32_t R, int32_t C);
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t st);
 
 // ---------------------------------------------------------------------------
