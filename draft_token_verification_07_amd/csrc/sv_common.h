@@ -88,47 +88,6 @@ __device__ __forceinline__ RowSplit row_split(const void *row, int32_t len) {
     return s;
 }
 
-// Visit the elements [lo_vec, hi_vec) of the vector body, plus the head when
-// `with_head` and the tail when `with_tail`, calling f(value, index) with
-// indices increasing per lane.  U vectors are loaded per lane before any is
-// used, so U * 16 bytes per lane are in flight.
-template <int DT, int U, int NT, typename F>
-__device__ __forceinline__ void stream_row(const void *row, const RowSplit &s, int32_t lo_vec,
-                                           int32_t hi_vec, bool with_head, bool with_tail, F &&f) {
-    using E = Elem<DT>;
-    const int tid = threadIdx.x;
-    if (with_head && tid < s.head) f(E::load(row, tid), tid);
-    const u32x4 *body = reinterpret_cast<const u32x4 *>(
-        reinterpret_cast<const char *>(row) + (size_t)s.head * E::kBytes);
-    int32_t v = lo_vec + tid;
-    // full iterations: every lane has U vectors
-    for (; v + (U - 1) * NT < hi_vec; v += U * NT) {
-        u32x4 buf[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load(&body[v + u * NT]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[E::kPerVec];
-            E::unpack(buf[u], x);
-            const int32_t i0 = s.head + (v + u * NT) * E::kPerVec;
-#pragma unroll
-            for (int k = 0; k < E::kPerVec; ++k) f(x[k], i0 + k);
-        }
-    }
-    // ragged last iteration
-    for (; v < hi_vec; v += NT) {
-        float x[E::kPerVec];
-        E::unpack(__builtin_nontemporal_load(&body[v]), x);
-        const int32_t i0 = s.head + v * E::kPerVec;
-#pragma unroll
-        for (int k = 0; k < E::kPerVec; ++k) f(x[k], i0 + k);
-    }
-    if (with_tail && tid < s.tail) {
-        const int32_t i = s.head + s.nvec * E::kPerVec + tid;
-        f(E::load(row, i), i);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Wave / workgroup reductions (wave64).
 // ---------------------------------------------------------------------------
@@ -206,14 +165,8 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 // vmcnt(0)) before the workgroup bumps the counter, and the last workgroup
 // issues its loads only after it has seen the counter.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void pub_u32(void *p, uint32_t v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void pub_u64(void *p, uint64_t v) {
     __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t sub_u32(const void *p) {
-    return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t sub_u64(const void *p) {
     return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

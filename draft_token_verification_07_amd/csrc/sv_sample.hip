@@ -103,30 +103,6 @@ __device__ __forceinline__ int32_t lower_bound_i32(const int32_t *v, int32_t n, 
 // ---------------------------------------------------------------------------
 
 template <int NT>
-__device__ __forceinline__ float wg_sum_f32(float v, float *s_tmp) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[threadIdx.x / kWave] = v;
-    __syncthreads();
-    float t = s_tmp[0];
-    for (int w = 1; w < NT / kWave; ++w) t += s_tmp[w];
-    __syncthreads();
-    return t;
-}
-
-template <int NT>
-__device__ __forceinline__ int32_t wg_sum_i32(int32_t v, int32_t *s_tmp) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) s_tmp[threadIdx.x / kWave] = v;
-    __syncthreads();
-    int32_t t = 0;
-    for (int w = 0; w < NT / kWave; ++w) t += s_tmp[w];
-    __syncthreads();
-    return t;
-}
-
-template <int NT>
 __device__ __forceinline__ int32_t wg_min_i32(int32_t v, int32_t *s_tmp) {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
@@ -597,17 +573,6 @@ __device__ SV_RARE void topp_exact_row(const void *row, int32_t L, float m, floa
 // exact and independent of the order of its terms.
 constexpr double kFixSelMaxMass = 60000.0;      // rows with more mass take the exact path
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
 // One step of a wave reduction on a 64-bit value: add the value DPP-moved
 // under control CTRL (rows outside ROWMASK add 0).  No LDS traffic.
 template <int CTRL, int ROWMASK>
@@ -726,15 +691,6 @@ __device__ __forceinline__ int32_t wave_append(bool pred, int32_t *counter) {
     base = __builtin_amdgcn_readlane(base, leader);
     return pred ? base + (int32_t)__popcll(bal & ((1ull << lane) - 1ull)) : -1;
 }
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint64_t w = __shfl_xor(v, o, kWave);
-        v = w < v ? w : v;
-    }
-    return v;
-}
-
 // Fixed-point weights of band tokens: w in (0, 1] becomes floor(w * 2^31),
 // so a u64 holds the exact sum of any band (at most 2048 tokens) and every
 // sum is independent of the order of its terms.
@@ -2048,23 +2004,6 @@ __device__ __forceinline__ uint64_t frac_floor(float u, uint64_t S) {
     if (sh >= 128) return 0;
     const unsigned __int128 pr = (unsigned __int128)m * S;
     return (uint64_t)(pr >> sh);
-}
-
-// Exclusive prefix of one u64 per thread in thread order, and the total.
-template <int NT>
-__device__ __forceinline__ uint64_t wg_excl_scan_u64(uint64_t v, uint64_t *s_tmp, uint64_t *total) {
-    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    const uint64_t inc = wave_incl_scan_u64(v);
-    if (lane == kWave - 1) s_tmp[w] = inc;
-    __syncthreads();
-    uint64_t base = 0, tot = 0;
-    for (int k = 0; k < NT / kWave; ++k) {
-        if (k < w) base += s_tmp[k];
-        tot += s_tmp[k];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + inc - v;
 }
 
 // One tile of a plain-mode draw, loaded: the vectors of target ids [t0, t1)
