@@ -42,6 +42,10 @@ template <> struct Elem<SV_F32> {
         o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
         o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
     }
+    // element k of a vector (k a compile-time constant after unrolling)
+    __device__ __forceinline__ static float elem(const u32x4 &v, int k) {
+        return __uint_as_float(k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w);
+    }
 };
 template <> struct Elem<SV_BF16> {
     static constexpr int kBytes = 2;
@@ -52,6 +56,10 @@ template <> struct Elem<SV_BF16> {
     __device__ __forceinline__ static void unpack(const u32x4 &v, float (&o)[kPerVec]) {
         o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
         o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+    __device__ __forceinline__ static float elem(const u32x4 &v, int k) {
+        const uint32_t w = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
+        return (k & 1) ? bf16_hi(w) : bf16_lo(w);
     }
 };
 

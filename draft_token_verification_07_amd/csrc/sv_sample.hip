@@ -1050,8 +1050,9 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
     // One iteration's U vectors per lane.  The running row maximum is shared
     // through LDS: a lane publishes (atomicMax on the key) only when its tile
     // maximum beats the shared value it read, rare after the first iteration.
-    auto tile = [&](const u32x4 (&raw)[U], const float (&xv)[U][E::kPerVec], const float (&vm)[U], float tm,
-                    int32_t vbase, int nu) {
+    // Elements are taken from the raw vectors where they are used (one
+    // shift or mask each), so only the U raw vectors are held per lane.
+    auto tile = [&](const u32x4 (&raw)[U], const float (&vm)[U], float tm, int32_t vbase, int nu) {
         if (tm > m_l) {
             s_l = (m_l == -INFINITY) ? 0.0f : s_l * exp2_hw((m_l - tm) * c);
             m_l = tm;
@@ -1061,7 +1062,7 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         for (int u = 0; u < U; ++u)
             if (u < nu) {
 #pragma unroll
-                for (int k = 0; k < E::kPerVec; ++k) s_l += exp2_hw(fmaf(xv[u][k], c, -mc));
+                for (int k = 0; k < E::kPerVec; ++k) s_l += exp2_hw(fmaf(E::elem(raw[u], k), c, -mc));
             }
         float smax = fkey_inv(s_maxkey);
         if (tm > smax) {
@@ -1080,12 +1081,17 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
                 }
             }
     };
+    auto vec_max = [&](const u32x4 &r) {
+        float v = E::elem(r, 0);
+#pragma unroll
+        for (int k = 1; k < E::kPerVec; ++k) v = fmaxf(v, E::elem(r, k));
+        return v;
+    };
     // A partial iteration (the first or the last): the loads are issued
     // unconditionally at clamped indices (a load under a divergent branch is
     // waited for inside it, one round trip per vector); vectors past the row
-    // are masked afterwards.  Requires sp.nvec >= 1.
-    auto load_iter = [&](int32_t it, u32x4 (&raw)[U], float (&xv)[U][E::kPerVec], float (&vm)[U],
-                         float &tm) -> int {
+    // (the last U - nu) are left out afterwards.  Requires sp.nvec >= 1.
+    auto load_iter = [&](int32_t it, u32x4 (&raw)[U], float (&vm)[U], float &tm) -> int {
         const int32_t vbase = it * U * NT + threadIdx.x;
 #pragma unroll
         for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[min(vbase + u * NT, sp.nvec - 1)]);
@@ -1094,13 +1100,7 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool ok = vbase + u * NT < sp.nvec;
-            E::unpack(raw[u], xv[u]);
-            vm[u] = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < E::kPerVec; ++k) {
-                if (!ok) xv[u][k] = -INFINITY;
-                vm[u] = fmaxf(vm[u], xv[u][k]);
-            }
+            vm[u] = ok ? vec_max(raw[u]) : -INFINITY;
             tm = fmaxf(tm, vm[u]);
             nu += ok ? 1 : 0;
         }
@@ -1112,12 +1112,12 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         // iteration 0: take the workgroup-wide maximum first, so the band
         // starts near the row maximum instead of each lane's own tile maximum
         u32x4 raw[U];
-        float xv[U][E::kPerVec], vm[U], tm;
-        const int nu = load_iter(0, raw, xv, vm, tm);
+        float vm[U], tm;
+        const int nu = load_iter(0, raw, vm, tm);
         const float wm = wave_max(tm);
         if ((threadIdx.x & (kWave - 1)) == 0 && wm > -INFINITY) atomicMax(&s_maxkey, zkey(wm));
         __syncthreads();
-        tile(raw, xv, vm, tm, threadIdx.x, nu);
+        tile(raw, vm, tm, threadIdx.x, nu);
     }
     // Waves with more of their row left issue first, so that rows sharing a
     // CU finish together instead of oldest-first: level floor(4 (full - it) /
@@ -1142,24 +1142,19 @@ __device__ __forceinline__ void topp_row(const void *row, int32_t L, float c, fl
         u32x4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[vbase + u * NT]);
-        float xv[U][E::kPerVec], vm[U];
+        float vm[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            E::unpack(raw[u], xv[u]);
-            vm[u] = xv[u][0];
-#pragma unroll
-            for (int k = 1; k < E::kPerVec; ++k) vm[u] = fmaxf(vm[u], xv[u][k]);
-        }
+        for (int u = 0; u < U; ++u) vm[u] = vec_max(raw[u]);
         float tm = vm[0];
 #pragma unroll
         for (int u = 1; u < U; ++u) tm = fmaxf(tm, vm[u]);
-        tile(raw, xv, vm, tm, vbase, U);
+        tile(raw, vm, tm, vbase, U);
     }
     if (iters > full && full > 0) {
         u32x4 raw[U];
-        float xv[U][E::kPerVec], vm[U], tm;
-        const int nu = load_iter(full, raw, xv, vm, tm);
-        tile(raw, xv, vm, tm, full * U * NT + threadIdx.x, nu);
+        float vm[U], tm;
+        const int nu = load_iter(full, raw, vm, tm);
+        tile(raw, vm, tm, full * U * NT + threadIdx.x, nu);
     }
     if (threadIdx.x < sp.tail) scalar_elem(E::load(row, sp.head + sp.nvec * E::kPerVec + threadIdx.x));
     // What follows is short and on the critical path, while other workgroups
