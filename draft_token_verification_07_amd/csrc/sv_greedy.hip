@@ -257,8 +257,14 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
                            dim3(kGreedyThreads), lds, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, true>), dim3(grid), dim3(kGreedyThreads), 0,
-                       st, a);
+    // Few workgroups (at most two per CU): twice the threads each, so that a
+    // CU keeps as many loads in flight as with more rows
+    if (grid <= kGreedyWideMaxWgs)
+        hipLaunchKernelGGL((greedy_kernel<DT, 2 * kGreedyThreads, kGreedyUnroll, true>), dim3(grid),
+                           dim3(2 * kGreedyThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, true>), dim3(grid), dim3(kGreedyThreads),
+                           0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((seq_kernel<kGreedyThreads>), dim3(a.B), dim3(kGreedyThreads), lds, st, a);

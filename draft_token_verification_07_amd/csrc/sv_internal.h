@@ -48,6 +48,7 @@ constexpr int kGreedyThreads = SV_GREEDY_THREADS;
 constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
 constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
 constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
+constexpr int kGreedyWideMaxWgs = 512;              // grids this small take 2 * kGreedyThreads per workgroup
 constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
 constexpr int kRowGroup = 8;                        // longer sequences end the row launch and walk in a second
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
