@@ -9,12 +9,14 @@
 //   is the argmax of the parent's row; the deepest accepted node wins (lowest
 //   index on ties); emit the root->winner path and the winner row's argmax.
 //
-// One launch.  Each row is cut into C contiguous chunks; one workgroup streams
-// one chunk once from HBM (16-byte loads, U vectors in flight per lane) and
-// keeps a per-lane (max, lowest index).  The chunk's argmax goes to the
-// workspace; the last workgroup of a sequence to arrive (atomic counter)
-// combines the chunks of every row in chunk order and runs the walk.  No host
-// synchronization; the time is the HBM read.
+// Each row is cut into C contiguous chunks; one workgroup streams one chunk
+// once from HBM (16-byte loads, U vectors in flight per lane) and keeps a
+// per-lane (max, lowest index).  Short chains of whole rows finish in one
+// launch: the last row of a sequence to arrive (atomic counter) combines the
+// row results and takes the first mismatch.  Trees, long chains and chunked
+// rows end the launch after the chunk results; a second launch with one
+// workgroup per sequence merges the chunks in chunk order and runs the chain
+// or the walk.  No host synchronization; the time is the HBM read.
 #include "sv_common.h"
 #include "sv_internal.h"
 
