@@ -262,8 +262,8 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
     // Few workgroups (at most two per CU): twice the threads each, so that a
     // CU keeps as many loads in flight as with more rows
     if (grid <= kGreedyWideMaxWgs)
-        hipLaunchKernelGGL((greedy_kernel<DT, 2 * kGreedyThreads, kGreedyUnroll, true>), dim3(grid),
-                           dim3(2 * kGreedyThreads), 0, st, a);
+        hipLaunchKernelGGL((greedy_kernel<DT, SV_GREEDY_WIDE * kGreedyThreads, kGreedyUnroll, true>), dim3(grid),
+                           dim3(SV_GREEDY_WIDE * kGreedyThreads), 0, st, a);
     else
         hipLaunchKernelGGL((greedy_kernel<DT, kGreedyThreads, kGreedyUnroll, true>), dim3(grid), dim3(kGreedyThreads),
                            0, st, a);

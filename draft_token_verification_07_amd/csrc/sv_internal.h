@@ -25,6 +25,9 @@ struct MaxSum;
 #ifndef SV_GREEDY_ITERS
 #define SV_GREEDY_ITERS 16
 #endif
+#ifndef SV_GREEDY_WIDE
+#define SV_GREEDY_WIDE 2
+#endif
 #ifndef SV_GREEDY_MIN_WGS
 #define SV_GREEDY_MIN_WGS 256
 #endif
@@ -48,7 +51,7 @@ constexpr int kGreedyThreads = SV_GREEDY_THREADS;
 constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
 constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
 constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
-constexpr int kGreedyWideMaxWgs = 512;              // grids this small take 2 * kGreedyThreads per workgroup
+constexpr int kGreedyWideMaxWgs = 512;              // grids this small take SV_GREEDY_WIDE * kGreedyThreads per workgroup
 constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
 constexpr int kRowGroup = 8;                        // longer sequences end the row launch and walk in a second
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
