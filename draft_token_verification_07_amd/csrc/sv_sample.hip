@@ -2345,7 +2345,6 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
 template <int DTT, int DTD, int NT>
 __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
     using DT = DrawTile<DTT, DTD, NT>;
-    constexpr int U = DT::U;
     constexpr int NW = NT / kWave;
     __shared__ float s_q[kTile];                  // rare fallback (zero residual mass)
     __shared__ uint64_t s_tmp[NW];
