@@ -52,7 +52,7 @@ def _load():
         lib.oracle_verify_sample.argtypes = [P, i32, P, i32, P, P, P, P, i32, i32, i32, i32,
                                              f64, f64, f64, P, P, P, P, P, P, P, P, i32]
         lib.oracle_row_dist.argtypes = [P, i32, i32, f64, f64, i32, P, P, P, P]
-        lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, P]
+        lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, C.c_double, P, P]
         lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
         lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
         _lib = lib
@@ -122,8 +122,10 @@ def row_dist(z, temperature, top_p, k_delta=0):
     return p, st, int(k[0]), float(lo[0]), float(hi[0])
 
 
-def chain_from_dists(P, Q, tokens, u_accept, u_sample):
-    """D3-D6 on given distributions P [g+1, V], Q [g, V] (float64)."""
+def chain_from_dists(P, Q, tokens, u_accept, u_sample, band=0.0):
+    """D3-D6 on given distributions P [g+1, V], Q [g, V] (float64).  Returns
+    (n, tokens [g+1], flags): flags are the boundary diagnostics of
+    verify_sample for the given band (0 with band = 0)."""
     P = np.ascontiguousarray(P, dtype=np.float64)
     g1, V = P.shape
     g = g1 - 1
@@ -131,11 +133,13 @@ def chain_from_dists(P, Q, tokens, u_accept, u_sample):
     tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(max(g, 1))
     ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(max(g, 1))
     out = np.empty(g + 1, np.int32)
+    fl = np.zeros(1, np.int32)
     n = _load().oracle_chain_from_dists(_ptr(P), _ptr(Q), _ptr(tok), _ptr(ua),
-                                        C.c_float(float(u_sample)), g, V, _ptr(out))
+                                        C.c_float(float(u_sample)), g, V, C.c_double(float(band)),
+                                        _ptr(out), _ptr(fl))
     if n < 0:
         raise MemoryError("oracle_chain_from_dists")
-    return n, out
+    return n, out, int(fl[0])
 
 
 def verify_greedy(logits, tokens):

@@ -415,24 +415,30 @@ int oracle_row_dist(const void *z, int dtype, int V, double T, double rho, int k
 
 /*
  * The chain and draw alone (D3-D6) on caller-provided distributions, for the
- * pins that integrate over the uniforms: P [gamma+1, V], Q [gamma, V].
- * Writes out_tokens [gamma+1], returns n (accepted count).
+ * pins that integrate over the uniforms and for parity accounting over many
+ * uniform sets: P [gamma+1, V], Q [gamma, V].  Writes out_tokens [gamma+1],
+ * returns n (accepted count).  When out_flags is not NULL it receives the
+ * boundary flags of verify_sample_seq with the same band: an evaluated
+ * decision with q > 0 and |u_i - p/q| < band, a draw with u_s within band of
+ * either edge of its CDF interval, a zero residual.
  */
 int oracle_chain_from_dists(const double *P, const double *Q, const int32_t *tokens,
                             const float *u_acc, float u_s, int gamma, int V,
-                            int32_t *out_tokens)
+                            double band, int32_t *out_tokens, int32_t *out_flags)
 {
     int n = gamma, i;
+    int32_t flags = 0;
     for (i = 0; i < gamma; ++i) {
         int32_t x = tokens[i];
         double a = 0.0, c = 0.0;
         if (x >= 0 && x < V) { a = P[(size_t)i * V + x]; c = Q[(size_t)i * V + x]; }
+        if (c > 0.0 && fabs((double)u_acc[i] - a / c) < band) flags |= ORC_FL_ACCEPT_EDGE;
         if (!((double)u_acc[i] * c < a)) { n = i; break; }
     }
     double *r = malloc(sizeof(double) * (size_t)V);
     if (!r) return -ORC_EMEM;
     const double *pn = P + (size_t)n * V;
-    int edge;
+    int edge = 0;
     int32_t pick;
     if (n < gamma) {
         double S = 0.0;
@@ -441,15 +447,21 @@ int oracle_chain_from_dists(const double *P, const double *Q, const int32_t *tok
             r[t] = d > 0.0 ? d : 0.0;
             S += r[t];
         }
-        pick = (S > 0.0) ? inverse_cdf(r, V, (double)u_s, 0.0, &edge)
-                         : inverse_cdf(pn, V, (double)u_s, 0.0, &edge);
+        if (S > 0.0) {
+            pick = inverse_cdf(r, V, (double)u_s, band, &edge);
+        } else {
+            flags |= ORC_FL_ZERO_RESID;
+            pick = inverse_cdf(pn, V, (double)u_s, band, &edge);
+        }
     } else {
-        pick = inverse_cdf(pn, V, (double)u_s, 0.0, &edge);
+        pick = inverse_cdf(pn, V, (double)u_s, band, &edge);
     }
+    if (edge) flags |= ORC_FL_CDF_EDGE;
     free(r);
     for (i = 0; i <= gamma; ++i) out_tokens[i] = -1;
     for (i = 0; i < n; ++i) out_tokens[i] = tokens[i];
     out_tokens[n] = pick;
+    if (out_flags) *out_flags = flags;
     return n;
 }
 

@@ -209,7 +209,7 @@ def _grid_measure_accept(oracle_mod, P, Q, x):
     """Measure of {u on the 2^-24 grid : the chain accepts x at position 0}."""
     lo, hi = 0, 1 << 24            # accept for u < lo/2^24 ... find first rejecting k
     def accepts(k):
-        n, _ = oracle_mod.chain_from_dists(P, Q, [x], [k / float(1 << 24)], 0.5)
+        n, _, _ = oracle_mod.chain_from_dists(P, Q, [x], [k / float(1 << 24)], 0.5)
         return n == 1
     if not accepts(0):
         return 0.0
@@ -228,7 +228,7 @@ def _grid_measure_accept(oracle_mod, P, Q, x):
 def _grid_measure_draw(oracle_mod, P, Q, x_reject, V):
     """Measure of u_s on the grid mapping to each token, after a forced rejection."""
     def pick(k):
-        _, out = oracle_mod.chain_from_dists(P, Q, [x_reject], [1.0 - 2.0 ** -24], k / float(1 << 24))
+        _, out, _ = oracle_mod.chain_from_dists(P, Q, [x_reject], [1.0 - 2.0 ** -24], k / float(1 << 24))
         return int(out[0])
     # first grid point whose pick is >= y, for every y (picks are monotone in u)
     first = np.zeros(V + 1, np.int64)
@@ -514,3 +514,43 @@ def test_threads_do_not_change_results(oracle_mod):
     b = oracle_mod.verify_sample(w["target"], w["draft"], w["tokens"], w["u_accept"], w["u_sample"], 0.8, 0.9, nthreads=4)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# --------------------------------------------------------------------------
+# The dense-row entry point (row_dist per row, then chain_from_dists) against
+# the batch entry point on the same inputs: identical tokens, lengths and
+# boundary flags.  This pins the flags chain_from_dists reports, which the
+# GPU parity accounting over many uniform sets relies on.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("top_p,d2t", [(1.0, False), (0.9, False), (1.0, True), (0.7, True)])
+def test_chain_from_dists_matches_verify_sample(oracle_mod, top_p, d2t):
+    rng = np.random.default_rng(7100 + int(top_p * 10) + 2 * d2t)
+    B, g, Vt = 24, 3, 97
+    Vd = 41 if d2t else Vt
+    dmap = np.sort(rng.choice(Vt, Vd, replace=False)).astype(np.int32) if d2t else None
+    zt = (rng.standard_normal((B, g + 1, Vt)) * 1.5).astype(np.float32)
+    zd = (rng.standard_normal((B, g, Vd)) * 1.5).astype(np.float32)
+    tok = rng.integers(0, Vt, (B, g)).astype(np.int32)
+    if d2t:                                   # most tokens on the map, some off it
+        tok[:, :2] = dmap[rng.integers(0, Vd, (B, 2))]
+    ua = synth.uniforms(rng, (B, g))
+    us = synth.uniforms(rng, (B,))
+    band = 1e-2                               # wide enough that some sequences are flagged
+    ref = oracle_mod.verify_sample(zt, zd, tok, ua, us, 0.9, top_p, d2t=dmap, band=band)
+    flagged = 0
+    for b in range(B):
+        P = np.stack([oracle_mod.row_dist(zt[b, i], 0.9, top_p)[0] for i in range(g + 1)])
+        Q = np.zeros((g, Vt))
+        for i in range(g):
+            q = oracle_mod.row_dist(zd[b, i], 0.9, top_p)[0]
+            if d2t:
+                Q[i, dmap] = q
+            else:
+                Q[i] = q
+        n, out, fl = oracle_mod.chain_from_dists(P, Q, tok[b], ua[b], us[b], band=band)
+        assert n == ref["accept_len"][b]
+        np.testing.assert_array_equal(out, ref["tokens"][b])
+        assert fl == ref["flags"][b], (b, fl, ref["flags"][b])
+        flagged += fl != 0
+    assert flagged > 0                        # the band is wide enough to exercise the flags
