@@ -11,23 +11,30 @@
 //   ascending token id.
 //
 // Launch structure (no host synchronization anywhere):
-//   top-p on:  one kernel.  One workgroup per row (target and draft rows)
-//     streams the row once, keeping the online max / sum-exp per lane and the
-//     tokens within a band of the running maximum in LDS; it then sorts that
-//     band (bitonic, LDS) by (logit desc, id asc), takes the cumulative mass
-//     in that order -- the page's _apply_top_p order -- and writes the kept
-//     set (boundary key, tie cut, kept mass, the kept ids and weights).  The
-//     last workgroup of each sequence to arrive runs the accept chain and
-//     draws from the kept list (a few dozen ids), so the rows are read once.
-//     Rows whose band is too crowded, or does not hold top_p of the mass,
-//     take an exact radix select over the whole row instead.
-//   top-p off: two kernels.  (1) Rows are cut into chunks; each workgroup
-//     streams one chunk and writes its (max, sum-exp); the last workgroup of a
-//     sequence combines them in chunk order, runs the accept chain and records
-//     n.  (2) Tiles of the row to draw from (target row n and draft row n, or
-//     the bonus row) are spread over workgroups; each sums its tile's weights;
-//     the last one scans the tile sums, finds the tile holding u_s * S and
-//     searches inside it.
+//   top-p on:  one kernel (topp_kernel).  One workgroup per row (target and
+//     draft rows) streams the row once, keeping the online max / sum-exp per
+//     lane and copying to LDS the 16-byte vectors whose largest logit lies
+//     within a band of the running maximum.  It then selects the kept set in
+//     exact fixed-point arithmetic: the band's tokens are binned by their
+//     distance below the row maximum, the bin whose inclusive mass first
+//     exceeds top_p * Z is found by a scan, and only that bin's tokens are
+//     ranked by (logit desc, id asc) -- the page's _apply_top_p order -- to
+//     find the last kept token.  The row publishes its kept set (boundary
+//     key, tie cut, kept mass, kept ids and weights).  The last workgroup of
+//     each sequence to arrive on the sequence's counter runs the accept chain
+//     and draws from the kept lists (a few dozen ids), so the rows are read
+//     once.  Rows the bins cannot settle take sub-band or radix selects, and
+//     rows whose band does not hold top_p of the mass take an exact radix
+//     select over the whole row.
+//   top-p off: three kernels in a row on the stream; each kernel boundary is
+//     the only synchronisation.  (1) stats_kernel: rows are cut into chunks,
+//     each workgroup streams one chunk and writes its (max, sum-exp), and one
+//     probe workgroup per sequence reads the logits at the draft tokens.
+//     (2) tile_kernel: one workgroup per (sequence, tile of target ids)
+//     merges the chunk results in chunk order, runs the accept chain, and
+//     sums the fixed-point residual (or bonus) weights of its tile of target
+//     row n.  (3) pick_kernel: one workgroup per sequence finds the tile
+//     holding u_s * S and the token inside it.
 #include <math.h>
 
 #include "sv_common.h"
@@ -1976,8 +1983,8 @@ __global__ __launch_bounds__(NT) void stats_kernel(SampleArgs a) {
 // inside it agree exactly whatever the order of the additions, and the draw
 // target floor(u * S) is exact.  Residual weights are F(max(0, p_t - q_t));
 // q_t comes from the draft row's vectors when it is laid out like the target
-// row, from a d2t scatter through LDS, or from single loads.  The last tile
-// workgroup of a sequence picks the tile and searches it.
+// row, from a d2t scatter through LDS, or from single loads.  pick_kernel
+// (one workgroup per sequence) then picks the tile and searches it.
 // ---------------------------------------------------------------------------
 
 // floor(w * 2^52) for 0 <= w < 2^11, from the bits of w (exact, no float64).
