@@ -1,4 +1,5 @@
-"""Parity accounting at full size over many uniform sets (sampling paths).
+"""Parity accounting at full size: many uniform sets (sampling paths), many
+batches (greedy and tree paths).
 
 A batch's p and q rows do not depend on the uniforms.  So the oracle computes
 each compared sequence's rows once: row_dist per row, with the d2t scatter
@@ -138,3 +139,33 @@ def test_parity_accounting_many_uniform_sets(oracle_mod, name, seed, S, sets):
     assert total >= 10000
     assert not bad, "%d sequences differ from the oracle: %s" % (len(bad), bad[:3])
     assert flagged <= 0.001 * total
+
+
+# ---------------------------------------------------------------------------
+# Greedy and tree paths take no uniforms: fresh full-size batches instead,
+# every one bit-exact (SSD guide sec. 7; the EAGLE blog's Match = True and
+# its sec. 5 tree).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seeds", [(3101, 3102, 3103, 3104)])
+def test_greedy_full_size_batches(oracle_mod, seeds):
+    from helpers import assert_same, run_greedy
+    n = 0
+    for s in seeds:
+        w = synth.greedy(s)                      # B=128, gamma=6, V=128256 bf16
+        assert_same(run_greedy(w), oracle_mod.verify_greedy(w["target"], w["tokens"]),
+                    ["tokens", "accept_len", "status"])
+        n += w["tokens"].shape[0]
+    _say("greedy: %d full-size sequences over %d batches, all bit-exact" % (n, len(seeds)))
+
+
+@pytest.mark.parametrize("seeds", [tuple(range(5101, 5117))])
+def test_tree_full_size_batches(oracle_mod, seeds):
+    from helpers import assert_same, run_tree
+    n = 0
+    for s in seeds:
+        w = synth.tree(s)                        # B=16, N=32, V=49152 bf16
+        assert_same(run_tree(w), oracle_mod.verify_tree_greedy(w["target"], w["tokens"], w["parents"]),
+                    ["path", "tokens", "accept_len", "status"])
+        n += w["tokens"].shape[0]
+    _say("tree: %d full-size trees over %d batches, all bit-exact" % (n, len(seeds)))
