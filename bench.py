@@ -10,11 +10,13 @@ its logits from HBM, not from the cache.
 
 Timing: after the warmup steps, the K timed steps are queued behind a short
 GPU sleep (so the host is ahead and the steps run back to back) and timed with
-one pair of HIP events on the launch stream; that gives `value` and
-`ms_per_step`.  The same K steps are then run once more with an event pair
-around every launch, which gives the mean launch duration used for the
-roofline (events between launches add a gap of a few microseconds each, so
-they are kept out of the throughput lap).
+one pair of HIP events on the launch stream.  That gives `value`,
+`ms_per_step`, and the mean launch duration the roofline divides by: the K
+launches run back to back, so total / K is the mean launch-to-launch time (for
+the multi-kernel paths, of the whole call).  The same K steps are then run once
+more with an event pair around every launch; those events add a gap of a
+microsecond or two per launch, so that lap is reported beside it
+(`config.launch_ms_*`) as a cross-check only.
 
 Prints ONE JSON line: verified vocab rows/s (target + draft rows per second),
 the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
@@ -276,7 +278,7 @@ def main():
     value = rows * K / (total_ms / 1e3)
     # Average launch duration: the throughput lap's events bracket K launches
     # that run back to back on the launch stream, so total / K is the mean
-    # launch-to-launch duration (for the two-kernel paths, of the call).  The
+    # launch-to-launch duration (for the multi-kernel paths, of the call).  The
     # per-launch lap, with events between launches, is reported beside it.
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     traffic = read_traffic(args.traffic_table, args.workload)
