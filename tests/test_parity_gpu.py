@@ -365,3 +365,49 @@ def test_full_sample_topp(oracle_mod):
 
 def test_full_sample_d2t(oracle_mod):
     _check_sample(oracle_mod, synth.eagle_d2t(4004), "full d2t")              # B=32, gamma=7, 128256 / 32000
+
+
+# ---------------------------------------------------------------------------
+# the documented limits: SV_MAX_GAMMA draft tokens, SV_MAX_TREE_NODES nodes,
+# SV_MAX_VOCAB ids per row
+# ---------------------------------------------------------------------------
+
+SV_MAX_GAMMA, SV_MAX_TREE_NODES, SV_MAX_VOCAB = 255, 4096, 1 << 24
+
+
+def test_max_gamma_greedy_and_sample(oracle_mod):
+    g = SV_MAX_GAMMA
+    w = synth.greedy(6101, B=3, gamma=g, V=1031, p_match=0.995)   # long accepted prefixes
+    _say("greedy max gamma", w["target"].shape)
+    out = run_greedy(w)
+    assert_same(out, oracle_mod.verify_greedy(w["target"], w["tokens"]), ["tokens", "accept_len", "status"])
+    assert out["accept_len"].max() > 64                  # positions past the first wave are reached
+    for top_p in (1.0, 0.9):
+        ws = synth.sample_topp(6102, B=2, gamma=g, V=1031, top_p=top_p)
+        # drafts equal to the target rows and each draft token its row's argmax
+        # (kept by any top-p): every draft is accepted, the chain runs to gamma
+        ws["draft"] = ws["target"][:, :g].copy()
+        ws["tokens"] = np.argmax(synth.bf16_to_f32(ws["target"][:, :g]), axis=-1).astype(np.int32)
+        s = _check_sample(oracle_mod, ws, "sample max gamma top_p=%g" % top_p)
+        assert (s["oracle"]["accept_len"] == g).all()
+
+
+def test_max_tree_nodes(oracle_mod):
+    N = SV_MAX_TREE_NODES
+    w = synth.tree(6103, B=2, N=N, V=257, max_depth=40, max_children=8, p_match=0.9)
+    _say("tree max nodes", w["target"].shape)
+    out = run_tree(w)
+    assert_same(out, oracle_mod.verify_tree_greedy(w["target"], w["tokens"], w["parents"]),
+                ["path", "tokens", "accept_len", "status"])
+    assert out["accept_len"].max() >= 5
+
+
+def test_max_vocab_greedy_and_sample(oracle_mod):
+    V = SV_MAX_VOCAB
+    w = synth.greedy(6104, B=1, gamma=1, V=V)
+    _say("greedy max vocab", w["target"].shape)
+    assert_same(run_greedy(w), oracle_mod.verify_greedy(w["target"], w["tokens"]), ["tokens", "accept_len", "status"])
+    # plain sampling: 512 chunks per row, chunk results beyond the LDS staging
+    # area, wave merges, and a pick over 8192 draw tiles
+    ws = synth.sample_plain(6105, B=1, gamma=1, V=V)
+    _check_sample(oracle_mod, ws, "sample max vocab")
