@@ -151,7 +151,7 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="sample_topp", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=2002)
