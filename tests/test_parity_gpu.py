@@ -411,3 +411,44 @@ def test_max_vocab_greedy_and_sample(oracle_mod):
     # area, wave merges, and a pick over 8192 draw tiles
     ws = synth.sample_plain(6105, B=1, gamma=1, V=V)
     _check_sample(oracle_mod, ws, "sample max vocab")
+
+
+# ---------------------------------------------------------------------------
+# concurrent calls on separate streams, each with its own workspace (the
+# header's contract): the launches go to the caller's stream only, and the
+# workspaces do not interact
+# ---------------------------------------------------------------------------
+
+def test_concurrent_streams_separate_workspaces(oracle_mod):
+    import torch
+    import draft_token_verification_07_amd as sv
+    from helpers import to_dev
+    wt = synth.sample_topp(6201, B=16, gamma=4, V=60013)
+    wp = synth.eagle_d2t(6202, B=8, gamma=5, Vt=40009, Vd=9001)
+    wg = synth.greedy(6203, B=24, gamma=6, V=70001)
+    dev = torch.device("cuda")
+    # inputs uploaded and made visible before any stream starts
+    it = [to_dev(wt[k]) for k in ("target", "draft", "tokens", "u_accept", "u_sample")]
+    ip = [to_dev(wp[k]) for k in ("target", "draft", "tokens", "u_accept", "u_sample", "d2t")]
+    ig = [to_dev(wg[k]) for k in ("target", "tokens")]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev) for _ in range(3)]       # default priority
+    outs = {}
+    for rep in range(3):
+        with torch.cuda.stream(streams[0]):
+            outs["t"] = sv.spec_verify_sample(*it, wt["temperature"], wt["top_p"])
+        with torch.cuda.stream(streams[1]):
+            outs["p"] = sv.spec_verify_sample(*ip[:5], wp["temperature"], wp["top_p"], d2t=ip[5])
+        with torch.cuda.stream(streams[2]):
+            outs["g"] = sv.spec_verify_greedy(*ig)
+        torch.cuda.synchronize()
+        _say("concurrent streams, repetition", rep)
+        for key, w in (("t", wt), ("p", wp)):
+            t, n, p, q, st = outs[key]
+            gpu = dict(tokens=t.cpu().numpy(), accept_len=n.cpu().numpy(), p_tok=p.cpu().numpy().astype(np.float64),
+                       q_tok=q.cpu().numpy().astype(np.float64), status=st.cpu().numpy())
+            s = compare_sample(w, gpu, oracle_mod)
+            assert s["boundary"] <= 1
+        t, n, st = outs["g"]
+        assert_same(dict(tokens=t.cpu().numpy(), accept_len=n.cpu().numpy(), status=st.cpu().numpy()),
+                    oracle_mod.verify_greedy(wg["target"], wg["tokens"]), ["tokens", "accept_len", "status"])
