@@ -452,3 +452,52 @@ def test_concurrent_streams_separate_workspaces(oracle_mod):
         t, n, st = outs["g"]
         assert_same(dict(tokens=t.cpu().numpy(), accept_len=n.cpu().numpy(), status=st.cpu().numpy()),
                     oracle_mod.verify_greedy(wg["target"], wg["tokens"]), ["tokens", "accept_len", "status"])
+
+
+# ---------------------------------------------------------------------------
+# optional outputs: out_p_tok, out_q_tok and out_status may be NULL; the
+# tokens and lengths are the same as with every output requested
+# ---------------------------------------------------------------------------
+
+def test_optional_outputs_null(oracle_mod):
+    import torch
+    import draft_token_verification_07_amd as sv
+    from helpers import to_dev
+    dev = torch.device("cuda")
+
+    def sample_both(w):
+        args = [to_dev(w[k]) for k in ("target", "draft", "tokens", "u_accept", "u_sample")]
+        d2t = to_dev(w["d2t"]) if w.get("d2t") is not None else None
+        full = sv.spec_verify_sample(*args, w["temperature"], w["top_p"], d2t=d2t)
+        B, g = w["tokens"].shape
+        bare = (torch.empty((B, g + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                None, None, None)
+        part = sv.spec_verify_sample(*args, w["temperature"], w["top_p"], d2t=d2t, out=bare)
+        torch.cuda.synchronize()
+        for k in (0, 1):
+            np.testing.assert_array_equal(full[k].cpu().numpy(), part[k].cpu().numpy())
+
+    _say("optional outputs NULL: top-p, plain, d2t")
+    sample_both(synth.sample_topp(6301, B=8, gamma=4, V=40009))
+    sample_both(synth.sample_plain(6302, B=6, gamma=3, V=30011))
+    sample_both(synth.eagle_d2t(6303, B=4, gamma=5, Vt=20011, Vd=5003))
+
+    _say("optional outputs NULL: greedy, tree")
+    w = synth.greedy(6304, B=16, gamma=6, V=50021)
+    t, n, _ = sv.spec_verify_greedy(to_dev(w["target"]), to_dev(w["tokens"].astype(np.int32)))
+    B, g = w["tokens"].shape
+    o = (torch.empty((B, g + 1), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev), None)
+    t2, n2, _ = sv.spec_verify_greedy(to_dev(w["target"]), to_dev(w["tokens"].astype(np.int32)), out=o)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(t.cpu().numpy(), t2.cpu().numpy())
+    np.testing.assert_array_equal(n.cpu().numpy(), n2.cpu().numpy())
+    w = synth.tree(6305, B=6, N=32, V=20011)
+    args = [to_dev(w["target"]), to_dev(w["tokens"].astype(np.int32)), to_dev(w["parents"].astype(np.int32))]
+    full = sv.spec_verify_tree_greedy(*args)
+    B, N = w["tokens"].shape
+    o = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+         torch.empty(B, dtype=torch.int32, device=dev), None)
+    part = sv.spec_verify_tree_greedy(*args, out=o)
+    torch.cuda.synchronize()
+    for k in (0, 1, 2):
+        np.testing.assert_array_equal(full[k].cpu().numpy(), part[k].cpu().numpy())
