@@ -2065,6 +2065,35 @@ struct DrawTile {
         }
         return s;
     }
+    // Slice u's vector when all its ids lie in [t0, t1) and in one subtile
+    // (2^sh ids): *sidx gets the subtile and *sum the weights' sum, and the
+    // per-id range checks and subtile bookkeeping of slice() are skipped.
+    // Returns false, with nothing done, for any other vector.
+    __device__ __forceinline__ bool slice_block(int u, const float *s_q, int sh, int *sidx, uint64_t *sum) const {
+        const int32_t v = v_lo + u * NT + (int32_t)threadIdx.x;
+        const int32_t i0 = sp.head + v * ET::kPerVec;
+        if (!(v < v_hi && i0 >= t0 && i0 + ET::kPerVec <= t1 &&
+              ((i0 - t0) >> sh) == ((i0 + ET::kPerVec - 1 - t0) >> sh)))
+            return false;
+        float zt[ET::kPerVec], zq[ET::kPerVec];
+        ET::unpack(rt[u], zt);
+        if constexpr (DTT == DTD) {
+            if (fused) ET::unpack(rd[u], zq);
+        }
+        uint64_t s = 0;
+#pragma unroll
+        for (int k = 0; k < ET::kPerVec; ++k) {
+            float q = 0.0f;
+            if (resid) {
+                if constexpr (DTT == DTD) q = fused ? qprob(zq[k]) : q_single(i0 + k, s_q);
+                else q = q_single(i0 + k, s_q);
+            }
+            s += weight_q(zt[k], q);
+        }
+        *sidx = (i0 - t0) >> sh;
+        *sum = s;
+        return true;
+    }
     // the ids of [t0, t1) outside the vector body (head or tail), one per
     // thread: thread i takes the i-th of them
     __device__ __forceinline__ int32_t edge_id() const {
@@ -2329,7 +2358,20 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
         acc += w;
     };
 #pragma unroll
-    for (int u = 0; u < U; ++u) (void)x.slice(u, s_q, add);
+    for (int u = 0; u < U; ++u) {
+        int sidx;
+        uint64_t sum;
+        if (x.slice_block(u, s_q, sh, &sidx, &sum)) {
+            if (sidx != cur) {
+                flush();
+                cur = sidx;
+                acc = 0;
+            }
+            acc += sum;
+        } else {
+            (void)x.slice(u, s_q, add);
+        }
+    }
     flush();
     const int32_t te = x.edge_id();
     if (te >= 0) {
