@@ -24,7 +24,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FLOAT32, BFLOAT16 = 0, 1
 
-ST_TOKEN_RANGE, ST_NO_MASS, ST_BAD_PARENT = 1, 4, 8
+ST_TOKEN_RANGE, ST_D2T, ST_NO_MASS, ST_BAD_PARENT = 1, 2, 4, 8
 FL_ACCEPT_EDGE, FL_CDF_EDGE, FL_ZERO_RESID = 1, 2, 4
 
 _lib = None
@@ -130,8 +130,11 @@ def chain_from_dists(P, Q, tokens, u_accept, u_sample, band=0.0):
     g1, V = P.shape
     g = g1 - 1
     Q = np.ascontiguousarray(Q if g > 0 else np.zeros((1, V)), dtype=np.float64)
-    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(max(g, 1))
-    ua = np.ascontiguousarray(u_accept, dtype=np.float32).reshape(max(g, 1))
+    tok = np.zeros(max(g, 1), np.int32)
+    ua = np.zeros(max(g, 1), np.float32)
+    if g > 0:
+        tok[:] = np.asarray(tokens, dtype=np.int32).reshape(g)
+        ua[:] = np.asarray(u_accept, dtype=np.float32).reshape(g)
     out = np.empty(g + 1, np.int32)
     fl = np.zeros(1, np.int32)
     n = _load().oracle_chain_from_dists(_ptr(P), _ptr(Q), _ptr(tok), _ptr(ua),

@@ -33,12 +33,13 @@
 /* Per-sequence status bits (documented meaning, defined independently of the
  * GPU library's header). */
 #define ORC_ST_TOKEN_RANGE 1  /* a draft / node token id outside [0, V)        */
+#define ORC_ST_D2T         2  /* d2t not strictly increasing, or an entry outside [0, Vt) */
 #define ORC_ST_NO_MASS     4  /* a row whose maximum logit is not finite       */
 #define ORC_ST_BAD_PARENT  8  /* tree parent outside [0, k) for node k >= 1    */
 
 /* Boundary flags returned next to the outputs (oracle-only diagnostics). */
 #define ORC_FL_ACCEPT_EDGE 1  /* |u_i - p/q| < band at an evaluated decision, q > 0 */
-#define ORC_FL_CDF_EDGE    2  /* u_s within band of either CDF edge of the sample   */
+#define ORC_FL_CDF_EDGE    2  /* u_s within band of an interior CDF edge of the sample */
 #define ORC_FL_ZERO_RESID  4  /* residual mass was exactly 0: sampled from p instead */
 
 /* Return codes. */
@@ -187,7 +188,11 @@ typedef struct {
  * [Ling tutorial] sec. 4.2 (torch.multinomial over the normalised weights).
  * Returns min{ j : sum_{t<=j} w_t > u * S } (strict, so zero-weight ids are
  * never drawn); if rounding leaves no such j, the last j with w_j > 0.
- * Sets *edge when u lies within band of either edge of the chosen interval.
+ * Sets *edge when u lies within band of an interior edge of the chosen
+ * interval: its lower edge when an id before the pick has positive weight,
+ * its upper edge when an id after it does.  The outer edges 0 and 1 are not
+ * decision boundaries (no other token lies beyond them), so they are never
+ * flagged.
  */
 static int32_t inverse_cdf(const double *w, int V, double u, double band, int *edge)
 {
@@ -211,7 +216,13 @@ static int32_t inverse_cdf(const double *w, int V, double u, double band, int *e
         before = S - (pick >= 0 ? w[pick] : 0.0);
         cum = S;
     }
-    *edge = (S > 0.0) && (fabs(u - before / S) < band || fabs(u - cum / S) < band);
+    int pos_before = 0, pos_after = 0;
+    for (j = 0; j < pick; ++j)
+        if (w[j] > 0.0) pos_before = 1;
+    for (j = pick + 1; pick >= 0 && j < V; ++j)
+        if (w[j] > 0.0) pos_after = 1;
+    *edge = (S > 0.0) && ((pos_before && fabs(u - before / S) < band) ||
+                          (pos_after && fabs(u - cum / S) < band));
     return pick;
 }
 
@@ -346,6 +357,8 @@ static void *sample_worker(void *arg)
  * Outputs: out_tokens [B, gamma+1] (-1 padded), out_len [B],
  *   out_p / out_q [B, gamma] (p_i(x_i), q_i(x_i) for every i; may be NULL),
  *   out_status [B] (ORC_ST_*; may be NULL), out_flags [B] (ORC_FL_*; may be NULL),
+ *   (a d2t map that is not strictly increasing inside [0, Vt) gives ORC_ST_D2T
+ *   on every sequence when gamma > 0, see above),
  *   out_margin [B, 2*gamma+1, 2] top-p margins per row, target rows first
  *   (may be NULL).  k_delta [B, 2*gamma+1] or NULL: per-row kept-count shifts.
  * band: the half-width of the boundary band for the flags (1e-5 in the tests).
@@ -363,10 +376,31 @@ int oracle_verify_sample(const void *tl, int tdt, const void *dl, int ddt,
     if (B < 0 || gamma < 0 || Vt < 1 || Vd < 1 || !(T > 0.0) || !(rho > 0.0)) return ORC_EARG;
     if (d2t == NULL && Vd != Vt) return ORC_EARG;
     if (B == 0) return ORC_OK;
-    if (d2t) {
+    if (d2t && gamma > 0) {
+        /* [SSD guide] sec. 6: d2t maps each draft id to a distinct target id;
+         * this library takes it sorted.  A map that is not strictly increasing
+         * or leaves [0, Vt) is reported, not used: every sequence gets
+         * ORC_ST_D2T, no token (-1), length 0 and zero probabilities. */
+        int bad = 0;
         for (int j = 0; j < Vd; ++j) {
-            if (d2t[j] < 0 || d2t[j] >= Vt) return ORC_EARG;
-            if (j > 0 && d2t[j] <= d2t[j - 1]) return ORC_EARG;
+            if (d2t[j] < 0 || d2t[j] >= Vt) bad = 1;
+            if (j > 0 && d2t[j] <= d2t[j - 1]) bad = 1;
+        }
+        if (bad) {
+            for (int b = 0; b < B; ++b) {
+                for (int i = 0; i <= gamma; ++i) out_tokens[(size_t)b * (gamma + 1) + i] = -1;
+                out_len[b] = 0;
+                for (int i = 0; i < gamma; ++i) {
+                    if (out_p) out_p[(size_t)b * gamma + i] = 0.0;
+                    if (out_q) out_q[(size_t)b * gamma + i] = 0.0;
+                }
+                if (out_status) out_status[b] = ORC_ST_D2T;
+                if (out_flags) out_flags[b] = 0;
+                if (out_margin)
+                    for (int r = 0; r < 2 * (2 * gamma + 1); ++r)
+                        out_margin[(size_t)b * 2 * (2 * gamma + 1) + r] = INFINITY;
+            }
+            return ORC_OK;
         }
     }
     if (nthreads < 1) nthreads = 1;

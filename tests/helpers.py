@@ -7,7 +7,8 @@ the GPU, float64 in the oracle):
     zeros (filtered or off-map tokens) are exact zeros on both sides.
   * integer outputs (tokens, accept_len, status) are bit-exact, except
     - a sequence the oracle flags because a uniform lies within BAND of an
-      accept threshold p/q or of an edge of the drawn token's CDF interval:
+      accept threshold p/q or of an interior edge of the drawn token's CDF
+      interval (an edge with another token of positive weight beyond it):
       it is counted as a boundary sequence (the budget is 0.1 %);
     - a row whose top-p cumulative lands within BAND of top_p: the kept
       count one lower / higher is equally admissible, and the GPU must match

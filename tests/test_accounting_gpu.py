@@ -12,11 +12,12 @@ Rules ("Ling-3.0-flash-dspark" tutorial sec. 3.1 and sec. 4.2, with the
 readings on decision boundaries and top-p cut margins):
   - the accepted length and the emitted tokens equal the oracle's;
   - except in sequences the oracle flags: a uniform within 1e-5 of an
-    evaluated accept ratio p/q, or of either CDF edge of the draw;
+    evaluated accept ratio p/q, or of an interior CDF edge of the draw;
   - and in sequences where a top-p cut lies within 1e-5 of top_p, whose
     outputs may instead follow an admissible neighbouring kept set;
-  - the sequences the boundary rule excuses (flagged, with integers that
-    differ) stay under 0.1% of all sequences compared.  Being inside the band
+  - the sequences either rule excuses (flagged with integers that differ, or
+    matching only an alternative kept set) stay under 0.1% of all sequences
+    compared.  Being inside the band
     alone is not the budgeted count: a row of V ids splits [0, 1) into V CDF
     intervals, so with V ~ 10^5 most draws land within 1e-5 of an edge of
     their own interval.  That count is reported for information.
@@ -138,7 +139,7 @@ def test_parity_accounting_many_uniform_sets(oracle_mod, name, seed, S, sets):
          "(%d inside the band in all)" % (total, exact, alternative, flagged, in_band))
     assert total >= 10000
     assert not bad, "%d sequences differ from the oracle: %s" % (len(bad), bad[:3])
-    assert flagged <= 0.001 * total
+    assert flagged + alternative <= 0.001 * total
 
 
 # ---------------------------------------------------------------------------

@@ -60,6 +60,125 @@ def test_golden_greedy(oracle_mod, case):
 
 
 # --------------------------------------------------------------------------
+# Boundary flags (hand-worked, tests/golden/hand_worked.json "boundary_cases").
+# These decide which GPU/oracle differences the parity tests excuse, so each
+# bit is shown set and clear on closed-form cases: exact dyadic p and q, and
+# uniforms 2^-18 (inside the 1e-5 band) or 2^-15 (outside it) from an accept
+# ratio or from a CDF edge.
+# --------------------------------------------------------------------------
+
+def _case_arrays(case):
+    tl = np.asarray(case["target_logits"], np.float32)[None]
+    g = tl.shape[1] - 1
+    V = tl.shape[2]
+    dl = (np.asarray(case["draft_logits"], np.float32)[None] if g > 0 else np.zeros((1, 0, V), np.float32))
+    tok = np.asarray(case["tokens"], np.int32).reshape(1, g)
+    ua = np.asarray(case["u_accept"], np.float32).reshape(1, g)
+    us = np.asarray([case["u_sample"]], np.float32)
+    return tl, dl, tok, ua, us
+
+
+def _equal_weight_dist(logits):
+    """Rows of equal logits and masked (-1e30) ids: uniform over the unmasked ids."""
+    m = np.asarray(logits, np.float64) > -1e29
+    return m / m.sum(axis=-1, keepdims=True)
+
+
+BOUNDARY_CASES = json.load(open(GOLDEN))["boundary_cases"]
+
+
+@pytest.mark.parametrize("case", BOUNDARY_CASES, ids=lambda c: c["name"])
+def test_golden_boundary_flags(oracle_mod, case):
+    tl, dl, tok, ua, us = _case_arrays(case)
+    out = oracle_mod.verify_sample(tl, dl, tok, ua, us, 1.0, 1.0, band=1e-5)
+    e = case["expect"]
+    assert out["tokens"][0].tolist() == e["tokens"]
+    assert int(out["accept_len"][0]) == e["accept_len"]
+    assert int(out["flags"][0]) == e["flags"], (int(out["flags"][0]), e["flags"])
+    # the dense-row entry point on the hand-derived distributions reports the same
+    P = _equal_weight_dist(case["target_logits"])
+    g = P.shape[0] - 1
+    Q = _equal_weight_dist(case["draft_logits"]) if g > 0 else np.zeros((0, P.shape[1]))
+    n, toks, fl = oracle_mod.chain_from_dists(P, Q, tok[0], ua[0], us[0], band=1e-5)
+    assert n == e["accept_len"] and toks.tolist() == e["tokens"] and fl == e["flags"]
+
+
+def test_boundary_flag_cases_cover_every_bit():
+    """Both flag bits appear set and clear among the hand-worked cases."""
+    seen = {(c["expect"]["flags"] & bit) != 0 for c in BOUNDARY_CASES for bit in (1,)}
+    assert seen == {True, False}
+    seen = {(c["expect"]["flags"] & bit) != 0 for c in BOUNDARY_CASES for bit in (2,)}
+    assert seen == {True, False}
+
+
+# --------------------------------------------------------------------------
+# Top-p alternatives within the band (hand-worked "topp_alternative_cases"):
+# the kept count, both margins, the kept set, and which id the k-1 / k+1
+# alternative drops or adds.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["topp_alternative_cases"], ids=lambda c: c["name"])
+def test_golden_topp_alternatives(oracle_mod, case):
+    z = _ln32(case["probs"])
+    e = case["expect"]
+    p, st, k, lo, hi = oracle_mod.row_dist(z, 1.0, case["top_p"])
+    assert st == 0 and k == e["k"]
+    assert abs(lo - e["margin_lo"]) < 1e-6 and abs(hi - e["margin_hi"]) < 1e-6
+    assert np.flatnonzero(p > 0).tolist() == e["kept"]
+    np.testing.assert_allclose(p, e["p"], atol=1e-6)
+    assert (lo < 1e-5) == (e["kept_minus"] is not None)
+    assert (hi < 1e-5) == (e["kept_plus"] is not None)
+    if e["kept_minus"] is not None:
+        pm = oracle_mod.row_dist(z, 1.0, case["top_p"], k_delta=-1)[0]
+        assert np.flatnonzero(pm > 0).tolist() == e["kept_minus"]
+        np.testing.assert_allclose(pm, e["p_minus"], atol=1e-6)
+    if e["kept_plus"] is not None:
+        pp = oracle_mod.row_dist(z, 1.0, case["top_p"], k_delta=1)[0]
+        assert np.flatnonzero(pp > 0).tolist() == e["kept_plus"]
+        np.testing.assert_allclose(pp, e["p_plus"], atol=1e-6)
+
+
+def test_k_delta_drops_and_adds_the_stable_order_neighbour(oracle_mod):
+    """k_delta = -1 removes exactly the id at sorted position k-1 and
+    k_delta = +1 adds exactly the id at position k, where the order is
+    numpy's lexsort by (logit descending, id ascending), on tie-heavy rows."""
+    rng = np.random.default_rng(41)
+    for trial in range(300):
+        V = int(rng.integers(3, 40))
+        z = rng.choice(np.array([-1.5, -0.5, 0.0, 0.5, 1.0, 2.0], np.float32), size=V)
+        rho = float(rng.uniform(0.05, 0.95))
+        p0, _, k, _, _ = oracle_mod.row_dist(z, 1.0, rho)
+        order = np.lexsort((np.arange(V), -z.astype(np.float64)))
+        assert set(np.flatnonzero(p0 > 0)) == set(order[:k].tolist())
+        if k >= 2:
+            pm = oracle_mod.row_dist(z, 1.0, rho, k_delta=-1)[0]
+            assert set(np.flatnonzero(pm > 0)) == set(order[:k - 1].tolist())
+        if k < V:
+            pp = oracle_mod.row_dist(z, 1.0, rho, k_delta=1)[0]
+            assert set(np.flatnonzero(pp > 0)) == set(order[:k + 1].tolist())
+
+
+def test_d2t_bad_map_sets_status_bit(oracle_mod):
+    """A d2t map that is not strictly increasing, or leaves [0, Vt), is
+    reported as status bit 2 on every sequence, and nothing is drawn."""
+    rng = np.random.default_rng(8)
+    B, g, Vt, Vd = 3, 2, 50, 10
+    zt = rng.standard_normal((B, g + 1, Vt)).astype(np.float32)
+    zd = rng.standard_normal((B, g, Vd)).astype(np.float32)
+    good = np.sort(rng.choice(Vt, Vd, replace=False)).astype(np.int32)
+    tok = good[rng.integers(0, Vd, (B, g))]
+    ua, us = synth.uniforms(rng, (B, g)), synth.uniforms(rng, (B,))
+    ok = oracle_mod.verify_sample(zt, zd, tok, ua, us, 1.0, 1.0, d2t=good)
+    assert (ok["status"] & oracle_mod.ST_D2T == 0).all()
+    for bad in (good[::-1].copy(), np.where(np.arange(Vd) == 4, Vt, good).astype(np.int32),
+                np.where(np.arange(Vd) == 0, -1, good).astype(np.int32),
+                np.where(np.arange(Vd) == 5, good[4], good).astype(np.int32)):
+        out = oracle_mod.verify_sample(zt, zd, tok, ua, us, 1.0, 1.0, d2t=bad)
+        assert (out["status"] == oracle_mod.ST_D2T).all()
+        assert (out["tokens"] == -1).all() and (out["accept_len"] == 0).all()
+
+
+# --------------------------------------------------------------------------
 # P1: q == p accepts every draft (accept probability min(1, p/q) = 1)
 # --------------------------------------------------------------------------
 
