@@ -21,7 +21,10 @@ microsecond or two per launch, so that lap is reported beside it
 Prints ONE JSON line: verified vocab rows/s (target + draft rows per second),
 the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
 launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
-the same workload.
+the same workload (one thread and every host core).  The default run then
+times the other four workloads the same way and reports each under
+config.workloads (step time, rows/s, GB/s and fraction of peak, counter
+traffic, the oracle's rows/s).
 """
 from __future__ import annotations
 
@@ -110,13 +113,23 @@ def device_sets(w, nrot, dev):
     return sets
 
 
-def cpu_baseline(w, max_seqs: int, work_seconds: float):
-    """Time the oracle as it stands on the first max_seqs sequences, with
-    every host core this process may use, repeating the pass until about
-    work_seconds of CPU time (wall time x threads used) have been spent."""
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, max_seqs: int, work_seconds: float, threads: int):
+    """Time the oracle as it stands on the first max_seqs sequences with
+    `threads` threads (sampling; the greedy and tree oracles are one
+    thread), repeating the pass until about work_seconds of CPU time (wall
+    time x threads used) have been spent."""
     import oracle
     oracle.build(force=False)
-    cores = min(len(os.sched_getaffinity(0)), 64)
     B = w["target"].shape[0]
     s = min(B, max_seqs)
     sl = slice(0, s)
@@ -125,8 +138,8 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float):
         if w["kind"] == "sample":
             oracle.verify_sample(w["target"][sl], w["draft"][sl], w["tokens"][sl], w["u_accept"][sl],
                                  w["u_sample"][sl], w["temperature"], w["top_p"], d2t=w.get("d2t"),
-                                 nthreads=cores)
-            return s * (2 * w["tokens"].shape[1] + 1), min(cores, s)
+                                 nthreads=threads)
+            return s * (2 * w["tokens"].shape[1] + 1), min(threads, s)
         if w["kind"] == "greedy":
             oracle.verify_greedy(w["target"][sl], w["tokens"][sl])
         else:
@@ -143,63 +156,38 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float):
         dt = time.perf_counter() - t0
         if dt * used >= work_seconds or dt >= 3.0 * work_seconds:
             break
-    return dict(value=rows / dt, unit="rows/s", cores=used, kind="oracle",
-                sample="%d pass(es) over the first %d of %d sequences of the same workload, %.2f s wall"
-                       % (passes, s, B, dt))
+    return dict(value=rows / dt, cores=used, passes=passes, seqs=s, wall_s=dt)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sample_topp", choices=sorted(WORKLOADS))
-    ap.add_argument("--seed", type=int, default=2002)
-    ap.add_argument("--cold-bytes", type=float, default=1.0e9,
-                    help="total bytes of rotated input copies (> 3x the 256 MB Infinity Cache)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=64)
-    ap.add_argument("--cpu-work-seconds", type=float, default=10.0,
-                    help="CPU time (wall x threads) to spend timing the oracle")
-    ap.add_argument("--queue-ahead-cycles", type=float, default=4e7,
-                    help="GPU sleep queued before the timed steps (lets the host run ahead)")
-    ap.add_argument("--copy-calibration", type=float, default=0.0,
-                    help="instead of the benchmark, copy this many bytes device-to-device "
-                         "(a kernel of known traffic, to scale rocprofv3 byte counters)")
-    ap.add_argument("--traffic-table", default=os.path.join(ROOT, "profiles", "hbm_traffic.md"),
-                    help="HBM bytes per launch measured with rocprofv3 counters (markdown table)")
-    args = ap.parse_args()
+def cpu_baselines(w, max_seqs: int, work_seconds: float):
+    """The oracle on one thread and on every host core this process may use."""
+    ncores = min(len(os.sched_getaffinity(0)), 64)
+    one = cpu_baseline(w, max(1, max_seqs // 8), work_seconds, 1)
+    many = cpu_baseline(w, max_seqs, work_seconds, ncores) if w["kind"] == "sample" and ncores > 1 else one
+    B = w["target"].shape[0]
+    return dict(value=many["value"], unit="rows/s", cores=many["cores"], kind="oracle",
+                value_1thread=one["value"], cores_available=ncores, nproc=os.cpu_count(), cpu_model=cpu_model(),
+                sample="1 thread: %d pass(es) over the first %d of %d sequences, %.2f s wall; "
+                       "%d threads: %d pass(es) over the first %d, %.2f s wall (same workload)"
+                       % (one["passes"], one["seqs"], B, one["wall_s"], many["cores"], many["passes"],
+                          many["seqs"], many["wall_s"]))
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this verification path shards by sequence with no "
-              "communication, and only --gpus 1 is run here.", file=sys.stderr)
-        sys.exit(2)
 
+KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
+               eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
+               tree="greedy_kernel+seq_kernel")
+
+
+def measure(name, args, dev, log):
+    """Time one workload: W warmup steps, then K steps twice (throughput lap,
+    then a lap with events around every launch).  Returns a dict."""
     import torch
-    if args.copy_calibration > 0:
-        n = int(args.copy_calibration) // 4
-        a = torch.ones(n, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=5)), flush=True)
-        return
     import draft_token_verification_07_amd as sv
-    from draft_token_verification_07_amd import binding as bnd
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    sv.lib()                                   # fails loudly without the HIP library
-
-    print("[bench] generating %s (seed %d)" % (args.workload, args.seed), file=sys.stderr, flush=True)
-    w = make_inputs(args.workload, args.seed)
+    log("[bench] generating %s (seed %d)" % (name, args.seed))
+    w = make_inputs(name, args.seed)
     nbytes = compulsory_bytes(w)
     nrot = max(1, int(math.ceil(args.cold_bytes / nbytes)))
-
     sets = device_sets(w, nrot, dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -216,7 +204,6 @@ def main():
         def step(s):
             sv.spec_verify_sample(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
                                   w["temperature"], w["top_p"], d2t=s["d2t"], ws=ws, out=outs)
-        kernel = "topp_kernel" if w["top_p"] < 1 else "stats_kernel+tile_kernel+pick_kernel"
     elif w["kind"] == "greedy":
         B, g = w["tokens"].shape
         need = sv.sv_workspace_bytes_greedy(B, g, w["target"].shape[2])
@@ -225,7 +212,6 @@ def main():
 
         def step(s):
             sv.spec_verify_greedy(s["target"], s["tokens"], ws=ws, out=outs)
-        kernel = "greedy_kernel"
     else:
         B, N = w["tokens"].shape
         need = sv.sv_workspace_bytes_tree(B, N, w["target"].shape[2])
@@ -234,9 +220,7 @@ def main():
 
         def step(s):
             sv.spec_verify_tree_greedy(s["target"], s["tokens"], s["parents"], ws=ws, out=outs)
-        kernel = "greedy_kernel+seq_kernel"
     ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-    del bnd
 
     for i in range(args.warmup):
         step(sets[i % nrot])
@@ -271,38 +255,115 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     per_launch_ms = [a.elapsed_time(b) for a, b in ev]
-    mean_launch_ms = float(np.mean(per_launch_ms))
+    del sets, ws, outs
+    torch.cuda.empty_cache()
 
     ms_per_step = total_ms / K
     rows = rows_per_step(w)
-    value = rows * K / (total_ms / 1e3)
     # Average launch duration: the throughput lap's events bracket K launches
     # that run back to back on the launch stream, so total / K is the mean
-    # launch-to-launch duration (for the multi-kernel paths, of the call).  The
-    # per-launch lap, with events between launches, is reported beside it.
+    # launch-to-launch duration (for the multi-kernel paths, of the call).
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
-    traffic = read_traffic(args.traffic_table, args.workload)
+    res = dict(workload=name, desc=WORKLOADS[name]["desc"], kernel=KERNELS[name],
+               logits_dtype=str(w["target"].dtype).replace("uint16", "bf16"),
+               rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
+               ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
+               seqs_per_s=float(w["target"].shape[0] * K / (total_ms / 1e3)),
+               achieved_GBps=achieved, frac=achieved / PEAK_GBS,
+               traffic=read_traffic(args.traffic_table, name),
+               launch_ms_mean=float(np.mean(per_launch_ms)), launch_ms_median=float(np.median(per_launch_ms)),
+               launch_ms_p10=float(np.percentile(per_launch_ms, 10)),
+               launch_ms_p90=float(np.percentile(per_launch_ms, 90)))
+    log("[bench] %s: %.2f us/step, %.0f GB/s (%.3f of peak)" % (name, ms_per_step * 1e3, achieved, achieved / PEAK_GBS))
+    return w, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sample_topp", choices=sorted(WORKLOADS),
+                    help="the workload of the headline value and roofline")
+    ap.add_argument("--only", action="store_true", help="time the headline workload alone")
+    ap.add_argument("--seed", type=int, default=2002)
+    ap.add_argument("--cold-bytes", type=float, default=1.0e9,
+                    help="total bytes of rotated input copies (> 3x the 256 MB Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=64)
+    ap.add_argument("--cpu-work-seconds", type=float, default=10.0,
+                    help="CPU time (wall x threads) to spend timing the oracle on the headline workload")
+    ap.add_argument("--cpu-work-seconds-other", type=float, default=3.0,
+                    help="the same for each of the other workloads")
+    ap.add_argument("--queue-ahead-cycles", type=float, default=4e7,
+                    help="GPU sleep queued before the timed steps (lets the host run ahead)")
+    ap.add_argument("--copy-calibration", type=float, default=0.0,
+                    help="instead of the benchmark, copy this many bytes device-to-device "
+                         "(a kernel of known traffic, to scale rocprofv3 byte counters)")
+    ap.add_argument("--traffic-table", default=os.path.join(ROOT, "profiles", "hbm_traffic.md"),
+                    help="HBM bytes per launch measured with rocprofv3 counters (markdown table)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this verification path shards by sequence with no "
+              "communication, and only --gpus 1 is run here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_read=4 * n, copy_bytes_written=4 * n, launches=5)), flush=True)
+        return
+    import draft_token_verification_07_amd as sv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.lib()                                   # fails loudly without the HIP library
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    head = args.workload
+    names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp")
+                                            if n != head])
+    results, inputs = {}, {}
+    for name in names:
+        inputs[name], results[name] = measure(name, args, dev, log)
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, args.cpu_seqs, args.cpu_work_seconds)
+        for name in names:
+            log("[bench] timing the CPU oracle on %s" % name)
+            secs = args.cpu_work_seconds if name == head else args.cpu_work_seconds_other
+            c = cpu_baselines(inputs[name], args.cpu_seqs, secs)
+            results[name]["cpu_rows_per_s"] = c["value"]
+            results[name]["cpu_rows_per_s_1thread"] = c["value_1thread"]
+            results[name]["cpu_threads"] = c["cores"]
+            if name == head:
+                cpu = c
 
-    dtype = "f32"
-    cfg = dict(workload=args.workload, desc=WORKLOADS[args.workload]["desc"],
-               logits_dtype=str(w["target"].dtype).replace("uint16", "bf16"),
-               rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
-               kernel=kernel, launch_ms_mean=mean_launch_ms,
-               launch_ms_median=float(np.median(per_launch_ms)),
-               launch_ms_p10=float(np.percentile(per_launch_ms, 10)),
-               launch_ms_p90=float(np.percentile(per_launch_ms, 90)),
-               step_GBps=float(nbytes / (ms_per_step / 1e3) / 1e9),
-               seqs_per_s=float(w["target"].shape[0] * K / (total_ms / 1e3)))
-    line = dict(metric=METRIC, value=value, unit="rows/s", n_gpus=1, steps=K, warmup=args.warmup,
-                ms_per_step=ms_per_step, higher_is_better=True, scaling="weak", vs_baseline=None,
-                dtype=dtype, data="synthetic", config=cfg,
-                roofline=dict(bound="hbm", achieved=achieved, peak=PEAK_GBS, unit="GB/s",
-                              frac=achieved / PEAK_GBS, traffic=traffic),
+    r = results[head]
+    K = args.steps
+    cfg = dict(workload=head, desc=r["desc"], logits_dtype=r["logits_dtype"], rows_per_step=r["rows_per_step"],
+               bytes_per_step=r["bytes_per_step"], rotated_input_copies=r["rotated_input_copies"],
+               kernel=r["kernel"], launch_ms_mean=r["launch_ms_mean"], launch_ms_median=r["launch_ms_median"],
+               launch_ms_p10=r["launch_ms_p10"], launch_ms_p90=r["launch_ms_p90"],
+               step_GBps=r["achieved_GBps"], seqs_per_s=r["seqs_per_s"],
+               workloads={n: {k: v for k, v in results[n].items() if k not in ("workload", "desc")}
+                          for n in names if n != head})
+    line = dict(metric=METRIC, value=r["rows_per_s"], unit="rows/s", n_gpus=1, steps=K, warmup=args.warmup,
+                ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="f32", data="synthetic", config=cfg,
+                roofline=dict(bound="hbm", achieved=r["achieved_GBps"], peak=PEAK_GBS, unit="GB/s",
+                              frac=r["frac"], traffic=r["traffic"]),
                 cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 

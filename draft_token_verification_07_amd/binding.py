@@ -29,7 +29,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
-SV_SEQ_TOKEN_RANGE, SV_SEQ_NO_MASS, SV_SEQ_BAD_PARENT = 1, 4, 8
+SV_SEQ_TOKEN_RANGE, SV_SEQ_D2T, SV_SEQ_NO_MASS, SV_SEQ_BAD_PARENT = 1, 2, 4, 8
 SV_MAX_GAMMA, SV_MAX_TREE_NODES, SV_MAX_VOCAB = 255, 4096, 1 << 24
 
 _STATUS = {0: "SV_OK", 1: "SV_ERR_INVALID_ARG", 2: "SV_ERR_UNSUPPORTED_DTYPE",

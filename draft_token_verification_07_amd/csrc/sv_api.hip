@@ -186,6 +186,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     char *base = static_cast<char *>(workspace);
     char *data = base + counter_region(workspace_bytes);
     a.cnt_stats = reinterpret_cast<uint32_t *>(base + L.cnt_stats);
+    a.map_flag = a.cnt_stats + B;
     a.seq = reinterpret_cast<SeqState *>(data + L.seq);
     a.rows = reinterpret_cast<RowDesc *>(data + L.rows);
     a.part = reinterpret_cast<MaxSum *>(data + L.part);

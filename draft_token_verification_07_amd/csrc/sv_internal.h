@@ -130,7 +130,7 @@ struct RowDesc {
     int32_t flags;    // RD_* bits
     float ptok;       // p (or q) of the row's draft token; 0 for the bonus row
 };
-enum { RD_NO_MASS = 1, RD_HAS_LIST = 2, RD_FALLBACK = 4 };
+enum { RD_NO_MASS = 1, RD_HAS_LIST = 2, RD_FALLBACK = 4, RD_BAD_MAP = 8 };
 
 struct KeptEnt {      // one kept id of a row and its weight w
     int32_t id;
@@ -165,6 +165,8 @@ struct SampleArgs {
     float *out_p, *out_q;
     // workspace
     uint32_t *cnt_stats;       // [B] (top-p)
+    uint32_t *map_flag;        // [1] after cnt_stats: nonzero once a plain-mode call sees a bad d2t map
+                               // (set by the probe workgroups, read by the draw tiles, cleared by the pick)
     SeqState *seq;             // [B]
     RowDesc *rows;             // [B, 2*gamma+1]: target rows then draft rows
     MaxSum *part;              // [B, (gamma+1)*Ct + gamma*Cd]

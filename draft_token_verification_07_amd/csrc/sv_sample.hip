@@ -1699,6 +1699,20 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
                                                                ((size_t)b * g + (r - g - 1)) * (size_t)a.Vd * Elem<DTD>::kBytes);
         const int32_t xt = tgt ? (r < g ? a.tokens[(size_t)b * g + r] : -1) : a.tokens[(size_t)b * g + (r - g - 1)];
         const int32_t *map = tgt ? nullptr : a.d2t;
+        // Draft row i checks slice i of the map (SSD guide sec. 6: strictly
+        // increasing target ids in [0, Vt)); the gamma slices cover every
+        // entry and step, and the epilogue reports a violation as SV_SEQ_D2T.
+        int map_bad = 0;
+        if (map) {
+            const int32_t i = r - g - 1;
+            const int32_t j0 = (int32_t)((int64_t)a.Vd * i / g), j1 = (int32_t)((int64_t)a.Vd * (i + 1) / g);
+            int bad = 0;
+            for (int32_t j = j0 + (int32_t)threadIdx.x; j < j1; j += NT) {
+                const int32_t cur = map[j], prev = j > 0 ? map[j - 1] : -1;
+                bad |= (cur < 0 || cur >= a.Vt || cur <= prev) ? 1 : 0;
+            }
+            map_bad = __syncthreads_or(bad);
+        }
         if constexpr (DTT == DTD) {
             topp_row<DTT, NT, U>(row, tgt ? a.Vt : a.Vd, a.c, band, a.top_p, rows + r, kept, s_cand, s_cvid, xt, map);
         } else {
@@ -1706,6 +1720,12 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
                 topp_row<DTT, NT, U>(row, a.Vt, a.c, band, a.top_p, rows + r, kept, s_cand, s_cvid, xt, map);
             else
                 topp_row<DTD, NT, U>(row, a.Vd, a.c, band, a.top_p, rows + r, kept, s_cand, s_cvid, xt, map);
+        }
+        if (map_bad && threadIdx.x == 0) {
+            // thread 0 published the descriptor: mark it
+            RowDesc d = sub(rows + r);
+            d.flags |= RD_BAD_MAP;
+            pub(rows + r, d);
         }
     }
 
@@ -1734,12 +1754,14 @@ __global__ __launch_bounds__(NT) SV_TOPP_OCCUPANCY void topp_kernel(SampleArgs a
     // draft token; n is the first position where u * q < p fails.
     int32_t status = 0, n = g;
     {
-        uint64_t nomass = 0;
+        uint64_t nomass = 0, badmap = 0;
         for (int32_t k0 = 0; k0 < NR; k0 += kWave) {
             const int32_t k = k0 + lane;
             nomass |= __ballot(k < NR && (s_rows[k].flags & RD_NO_MASS) != 0);
+            badmap |= __ballot(k < NR && (s_rows[k].flags & RD_BAD_MAP) != 0);
         }
         if (nomass) status |= SV_SEQ_NO_MASS;
+        if (badmap) status |= SV_SEQ_D2T;
         for (int32_t i0 = 0; i0 < g; i0 += kWave) {
             const int32_t i = i0 + lane;
             int32_t t = ti;
@@ -1926,18 +1948,27 @@ __device__ __forceinline__ void probe_tokens(const SampleArgs &a, int32_t b) {
 // d2t[j] >= k * tile, k = 0..ntiles.  Entry j (0 <= j <= Vd) owns the k with
 // d2t[j-1] < k * tile <= d2t[j] (d2t[-1] = -1, d2t[Vd] = +inf); the probe
 // workgroup of sequence b takes the j in [b (Vd+1) / B, (b+1) (Vd+1) / B).
+//
+// The same pass checks the map (SSD guide sec. 6: d2t sends draft id j to a
+// distinct target id; this library takes it strictly increasing in
+// [0, Vt)): entry j must lie in [0, Vt) and above entry j - 1.  The B slices
+// cover every entry and every step once; a violation sets the call's map
+// flag, which the draw tiles turn into SV_SEQ_D2T on every sequence.
 template <int NT>
 __device__ __forceinline__ void tile_bounds(const SampleArgs &a, int32_t b) {
     const int64_t n1 = (int64_t)a.Vd + 1;
     const int32_t j0 = (int32_t)(n1 * b / a.B), j1 = (int32_t)(n1 * (b + 1) / a.B);
+    bool bad = false;
     for (int32_t j = j0 + (int32_t)threadIdx.x; j < j1; j += NT) {
         const int64_t prev = j > 0 ? (int64_t)a.d2t[j - 1] : -1;
         const int64_t cur = j < a.Vd ? (int64_t)a.d2t[j] : INT64_MAX;
+        if (j < a.Vd && (cur < 0 || cur >= a.Vt || cur <= prev)) bad = true;
         const int64_t klo = prev < 0 ? 0 : prev / a.tile + 1;
         int64_t khi = cur / a.tile;
         if (khi > a.ntiles) khi = a.ntiles;
         for (int64_t k = klo; k <= khi; ++k) a.tile_jb[k] = j;
     }
+    if (bad && a.gamma > 0) atomicOr(a.map_flag, 1u);
 }
 
 // Plain mode, first launch.  Grid: B probe workgroups, then
@@ -2024,12 +2055,18 @@ struct DrawTile {
     u32x4 rt[U], rd[U];
 
     // Weight of target id t (fixed point) given its target logit and q.
+    // Contraction is off in both: the tile pass and the pick must compute the
+    // same float for every id, whether q arrives through LDS or inline.
     __device__ __forceinline__ uint64_t weight_q(float zt, float q) const {
+#pragma clang fp contract(off)
         const float p = nomass ? 0.0f : exp2_hw((zt - mp) * c) * izp;
         if (!resid) return fix52(p);
         return fix52(p - q > 0.0f ? p - q : 0.0f);
     }
-    __device__ __forceinline__ float qprob(float zq) const { return exp2_hw((zq - mq) * c) * izq; }
+    __device__ __forceinline__ float qprob(float zq) const {
+#pragma clang fp contract(off)
+        return exp2_hw((zq - mq) * c) * izq;
+    }
 
     // q of target id t when it does not come with the vectors
     __device__ __forceinline__ float q_single(int32_t t, const float *s_q) const {
@@ -2234,9 +2271,11 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
         ua = (double)a.u_acc[(size_t)b * g + i];
     }
     int32_t j0 = 0, j1 = 0;
+    uint32_t map_bad = 0;
     if (a.d2t) {
         j0 = min(max(a.tile_jb[k], 0), a.Vd);
         j1 = min(max(a.tile_jb[k + 1], j0), a.Vd);
+        if (k == 0 && threadIdx.x == 0) map_bad = a.map_flag[0];
     }
     __syncthreads();
     // Rows of few chunks are merged by one thread each, chunk by chunk in
@@ -2323,6 +2362,7 @@ __global__ __launch_bounds__(NT) void tile_kernel(SampleArgs a) {
         __syncthreads();
         if (k == 0 && threadIdx.x == 0) {
             int32_t status = (s_flags & 1) ? SV_SEQ_TOKEN_RANGE : 0;
+            if (map_bad) status |= SV_SEQ_D2T;
             for (int32_t r = 0; r < NR; ++r)
                 if (s_rows[r].flags & RD_NO_MASS) status |= SV_SEQ_NO_MASS;
             SeqState st;
@@ -2410,6 +2450,8 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
     const int32_t g = a.gamma;
     const int32_t b = blockIdx.x;
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    // every draw tile has read the map flag (previous launch): clear it for the next call
+    if (b == 0 && threadIdx.x == 0 && a.d2t) a.map_flag[0] = 0u;
     const SeqState *st = &a.seq[b];
     const int32_t n = st->n;
     const RowDesc dp = load_desc(&st->dp), dq = load_desc(&st->dq);
@@ -2528,7 +2570,13 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
                 const uint64_t w = v ? x.weight_q(zt, q) : 0ull;
                 const uint64_t inc = wave_incl_scan_u64_dpp(w);
                 const uint64_t hb = __ballot(w > 0 && inc > tin2 && inc - w <= tin2);
-                if (lane == 0 && hb) s_tok = ts + __ffsll((unsigned long long)hb) - 1;
+                // The weights are those the tile pass summed (same helpers, no
+                // contraction), so one id brackets tin2; should none, the
+                // subtile's last id of positive weight is drawn, the rule for
+                // a draw that rounding leaves without a crossing.
+                const uint64_t pb = __ballot(w > 0);
+                if (lane == 0 && (hb || pb))
+                    s_tok = hb ? ts + __ffsll((unsigned long long)hb) - 1 : ts + 63 - __clzll((long long)pb);
             }
             __syncthreads();
             tok = s_tok;
@@ -2594,7 +2642,7 @@ bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt,
     const int32_t tl = draw_tile(B, Vt);
     const int32_t nt = (Vt + tl - 1) / tl;
     L->cnt_stats = 0;
-    L->counter_bytes = align256(sizeof(uint32_t) * (size_t)B);
+    L->counter_bytes = align256(sizeof(uint32_t) * ((size_t)B + 1));     // arrival counters, then the map flag
     size_t off = 0;
     L->seq = off;       off = align256(off + sizeof(SeqState) * (size_t)B);
     L->rows = off;      off = align256(off + sizeof(RowDesc) * (size_t)B * NR);

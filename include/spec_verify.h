@@ -87,6 +87,9 @@ typedef enum {
 
 /* out_status bits (per sequence). */
 #define SV_SEQ_TOKEN_RANGE 1  /* a draft/node token id outside [0, V): treated as p = q = 0 (rejected / unmatched) */
+#define SV_SEQ_D2T         2  /* sampling with d2t and gamma > 0: the map is not strictly increasing inside
+                                 [0, Vt) (SSD guide sec. 6); set on every sequence, whose other outputs are
+                                 then unspecified (tokens still lie in [-1, Vt))                              */
 #define SV_SEQ_NO_MASS     4  /* a logits row whose maximum is not finite; draws from it return -1             */
 #define SV_SEQ_BAD_PARENT  8  /* tree: parents[b][k] outside [0, k) for k >= 1; that node is never accepted     */
 
@@ -115,8 +118,10 @@ size_t sv_workspace_bytes_tree(int32_t B, int32_t N, int32_t V);
  *   draft_tokens   [B, gamma] int32, TARGET-vocabulary ids.  May be NULL when gamma == 0.
  *   d2t            [Vd] int32, strictly increasing ids in [0, Vt): draft id j
  *                  is target id d2t[j].  NULL means Vd == Vt and the identity.
- *                  (A map that is not strictly increasing or leaves [0, Vt) is
- *                  outside the contract: results are undefined, memory safe.)
+ *                  The kernels check the map on every call with gamma > 0: one
+ *                  that is not strictly increasing or leaves [0, Vt) sets
+ *                  SV_SEQ_D2T on every sequence (memory stays safe; the other
+ *                  outputs are unspecified, tokens in [-1, Vt)).
  *   u_accept       [B, gamma] float32 in [0, 1).  May be NULL when gamma == 0.
  *   u_sample       [B] float32 in [0, 1).
  *   temperature    > 0 and finite (temperature 0 is spec_verify_greedy).

@@ -501,3 +501,76 @@ def test_optional_outputs_null(oracle_mod):
     torch.cuda.synchronize()
     for k in (0, 1, 2):
         np.testing.assert_array_equal(full[k].cpu().numpy(), part[k].cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# d2t maps that break the contract (SSD guide sec. 6: strictly increasing
+# target ids in [0, Vt)): every sequence reports SV_SEQ_D2T, tokens stay in
+# [-1, Vt), and a later call with a good map on the same workspace is clean
+# again (the plain path's map flag is cleared by each call)
+# ---------------------------------------------------------------------------
+
+def _bad_maps(d2t, Vt):
+    Vd = d2t.shape[0]
+    idx = np.arange(Vd)
+    return {
+        "reversed": d2t[::-1].copy(),
+        "entry_ge_Vt": np.where(idx == Vd // 2, Vt, d2t).astype(np.int32),
+        "negative": np.where(idx == 0, -5, d2t).astype(np.int32),
+        "repeat": np.where(idx == Vd - 1, d2t[Vd - 2], d2t).astype(np.int32),
+        "local_swap": np.where(idx == 7, d2t[8], np.where(idx == 8, d2t[7], d2t)).astype(np.int32),
+    }
+
+
+@pytest.mark.parametrize("top_p", [1.0, 0.9])
+def test_sample_d2t_bad_map_status(oracle_mod, top_p):
+    import torch
+    import draft_token_verification_07_amd as sv
+    B, g, Vt, Vd = 6, 3, 20011, 5003
+    w = synth.eagle_d2t(7701, B=B, gamma=g, Vt=Vt, Vd=Vd)
+    w["top_p"] = top_p
+    need = sv.sv_workspace_bytes_sample(B, g, Vt, Vd, top_p)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for name, bad in _bad_maps(w["d2t"], Vt).items():
+        _say("bad d2t map", name, "top_p", top_p)
+        wb = dict(w)
+        wb["d2t"] = bad
+        out = run_sample(wb, ws=ws)
+        orc = oracle_mod.verify_sample(wb["target"], wb["draft"], wb["tokens"], wb["u_accept"], wb["u_sample"],
+                                       wb["temperature"], top_p, d2t=bad)
+        assert (orc["status"] & oracle_mod.ST_D2T).all()
+        assert (out["status"] & sv.SV_SEQ_D2T).all(), (name, out["status"])
+        assert ((out["tokens"] >= -1) & (out["tokens"] < Vt)).all()
+        assert ((out["accept_len"] >= 0) & (out["accept_len"] <= g)).all()
+        # the same workspace, a good map: no status bit, parity as usual
+        good = run_sample(w, ws=ws)
+        assert not (good["status"] & sv.SV_SEQ_D2T).any()
+        compare_sample(w, good, oracle_mod)
+
+
+def test_sample_d2t_bad_map_gamma0_unchecked(oracle_mod):
+    """With gamma = 0 no draft row exists and the map is not used: no bit."""
+    w = synth.eagle_d2t(7702, B=3, gamma=0, Vt=9001, Vd=1001)
+    w["d2t"] = w["d2t"][::-1].copy()
+    out = run_sample(w)
+    assert (out["status"] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# the fp32-target / bf16-draft pair (the other mixed pair, bf16 target /
+# fp32 draft, is the EAGLE workload): with and without top-p and d2t
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("top_p,use_d2t", [(1.0, False), (0.9, False), (1.0, True), (0.8, True)])
+def test_sample_fp32_target_bf16_draft(oracle_mod, top_p, use_d2t):
+    if use_d2t:
+        w = synth.eagle_d2t(7801, B=6, gamma=4, Vt=40009, Vd=9001)
+        w["target"] = synth.bf16_to_f32(w["target"])
+        w["draft"] = synth.bf16_bits(w["draft"])
+    else:
+        w = synth.sample_plain(7802, B=6, gamma=4, V=40009)
+        w["draft"] = synth.bf16_bits(w["draft"])
+    w["top_p"] = top_p
+    w["temperature"] = 0.9
+    assert w["target"].dtype == np.float32 and w["draft"].dtype == np.uint16
+    _check_sample(oracle_mod, w, "fp32 target / bf16 draft, d2t=%s" % use_d2t)
