@@ -8,6 +8,7 @@ calling any entry point without it raises.
     tokens, accept_len, p_tok, q_tok, status = spec_verify_sample(
         target_logits, draft_logits, draft_tokens, u_accept, u_sample,
         temperature, top_p, d2t=None)
+    tokens, accept_len, p_tok, q_tok, status = spec_verify_sample_noalloc(..., out=outputs)
     tokens, accept_len, status = spec_verify_greedy(target_logits, draft_tokens)
     path, tokens, accept_len, status = spec_verify_tree_greedy(target_logits, node_tokens, parents)
 
@@ -72,6 +73,9 @@ def lib() -> C.CDLL:
                                                  C.c_float, C.c_float, P, P, P, P, P, P, sz, P]
                 L.spec_verify_greedy.restype = C.c_int
                 L.spec_verify_greedy.argtypes = [P, C.c_int, P, i32, i32, i32, P, P, P, P, sz, P]
+                L.spec_verify_sample_noalloc.restype = C.c_int
+                L.spec_verify_sample_noalloc.argtypes = [P, C.c_int, P, C.c_int, P, P, P, P, i32, i32, i32, i32,
+                                                         C.c_float, C.c_float, P, P, P, P, P, P]
                 L.spec_verify_tree_greedy.restype = C.c_int
                 L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
                 _lib = L
@@ -189,6 +193,46 @@ def spec_verify_sample(target_logits, draft_logits, draft_tokens, u_accept, u_sa
         _ptr(out_tokens), _ptr(out_len), _ptr(out_p), _ptr(out_q), _ptr(out_status),
         _ptr(ws), ws.numel(), _stream(dev))
     _raise("spec_verify_sample", rc)
+    return out_tokens, out_len, out_p, out_q, out_status
+
+
+def spec_verify_sample_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                               temperature: float, top_p: float, d2t=None, *, out):
+    """spec_verify_sample without a workspace: the library's static per-GPU
+    scratch is used and nothing is allocated.  The outputs are the caller's:
+    out = (tokens [B, g+1] int32, accept_len [B] int32, p_tok [B, g] float32
+    or None, q_tok [B, g] float32 or None, status [B] int32 or None)."""
+    L = lib()
+    dev = target_logits.device
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, gamma+1, Vt]")
+    B, g1, Vt = target_logits.shape
+    g = g1 - 1
+    _check(target_logits, "target_logits", dev)
+    tdt = _dtype_code(target_logits)
+    if g > 0:
+        _check(draft_logits, "draft_logits", dev)
+        if draft_logits.dim() != 3 or tuple(draft_logits.shape[:2]) != (B, g):
+            raise ValueError("draft_logits must be [B, gamma, Vd]")
+        Vd = draft_logits.shape[2]
+        ddt = _dtype_code(draft_logits)
+        _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, g))
+        _check(u_accept, "u_accept", dev, torch.float32, (B, g))
+    else:
+        Vd = Vt if d2t is None else d2t.shape[0]
+        ddt = tdt if draft_logits is None else _dtype_code(draft_logits)
+    _check(u_sample, "u_sample", dev, torch.float32, (B,))
+    if d2t is not None:
+        _check(d2t, "d2t", dev, torch.int32, (Vd,))
+    out_tokens, out_len, out_p, out_q, out_status = out
+    _check(out_tokens, "out_tokens", dev, torch.int32, (B, g + 1))
+    _check(out_len, "out_accept_len", dev, torch.int32, (B,))
+    rc = L.spec_verify_sample_noalloc(
+        _ptr(target_logits), tdt, _ptr(draft_logits if g > 0 else None), ddt,
+        _ptr(draft_tokens if g > 0 else None), _ptr(d2t), _ptr(u_accept if g > 0 else None), _ptr(u_sample),
+        B, g, Vt, Vd, float(temperature), float(top_p),
+        _ptr(out_tokens), _ptr(out_len), _ptr(out_p), _ptr(out_q), _ptr(out_status), _stream(dev))
+    _raise("spec_verify_sample_noalloc", rc)
     return out_tokens, out_len, out_p, out_q, out_status
 
 

@@ -5,10 +5,54 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sv_common.h"
 #include "sv_internal.h"
 
 using namespace sv;
+
+// Scratch of the allocation-free entry point: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol; kernels receive the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Zero the counter region of the scratch array (a fill kernel rather than a
+// memset, so that a caller capturing the stream records a kernel node).
+__global__ void scratch_clear(u32x4 *p, size_t n) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = z;
+}
+
+// The current device's scratch address, set up on the first call on that
+// device: the symbol's address for this device, then its counter region
+// cleared on `stream` (every call returns the counters to zero after that).
+sv_status scratch_for_current_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SV_ERR_HIP;
+    if (dev >= kMaxDevices) return SV_ERR_TOO_LARGE;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SV_ERR_HIP;
+        const size_t n = counter_region(SV_NOALLOC_SCRATCH_BYTES) / sizeof(u32x4);
+        hipLaunchKernelGGL(scratch_clear, dim3(256), dim3(256), 0, stream, static_cast<u32x4 *>(ptr), n);
+        if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -198,6 +242,28 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.tile_jb = reinterpret_cast<int32_t *>(data + L.tile_jb);
 
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status spec_verify_sample_noalloc(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
+                                     sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
+                                     const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,
+                                     int32_t Vt, int32_t Vd, float temperature, float top_p, int32_t *out_tokens,
+                                     int32_t *out_accept_len, float *out_p_tok, float *out_q_tok,
+                                     int32_t *out_status, hipStream_t stream) {
+    // sizes first: a call the scratch cannot hold fails before any set-up
+    const size_t need = sv_workspace_bytes_sample(B, gamma, Vt, Vd, top_p);
+    if (need > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_TOO_LARGE;
+    if (B == 0 || need == 0)            // nothing to do, or invalid sizes: the checks of the allocating variant
+        return spec_verify_sample(target_logits, target_dtype, draft_logits, draft_dtype, draft_tokens, d2t,
+                                  u_accept, u_sample, B, gamma, Vt, Vd, temperature, top_p, out_tokens,
+                                  out_accept_len, out_p_tok, out_q_tok, out_status, nullptr, 0, stream);
+    void *ws = nullptr;
+    const sv_status st = scratch_for_current_device(stream, &ws);
+    if (st != SV_OK) return st;
+    // always the whole array, so the counter region sits at the same place in every call
+    return spec_verify_sample(target_logits, target_dtype, draft_logits, draft_dtype, draft_tokens, d2t, u_accept,
+                              u_sample, B, gamma, Vt, Vd, temperature, top_p, out_tokens, out_accept_len, out_p_tok,
+                              out_q_tok, out_status, ws, SV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -189,6 +189,36 @@ sv_status spec_verify_tree_greedy(
     int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
     int32_t *out_status, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Sampling verification without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, outputs and results are those
+ * of spec_verify_sample; the scratch is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.
+ *   - Set-up, on the first call on a device: the array's address is looked up
+ *     and its counter region cleared by a small kernel on `stream`.  The call
+ *     allocates nothing (no hipMalloc / hipFree) and never synchronizes.
+ *   - Every call on one GPU shares that GPU's array and returns its counters
+ *     to zero; calls that may overlap on one GPU (different streams, host
+ *     threads) race and must be serialized by the caller.
+ *   - A call whose sv_workspace_bytes_sample() exceeds
+ *     SV_NOALLOC_SCRATCH_BYTES returns SV_ERR_TOO_LARGE with no launch (e.g.
+ *     B = 128, gamma = 5, Vt = Vd = 151936 with top-p fits; B = 256 does not).
+ * Errors: those of spec_verify_sample, SV_ERR_TOO_LARGE as above, SV_ERR_HIP
+ * when the scratch address cannot be obtained.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sv_status spec_verify_sample_noalloc(
+    const void *target_logits, sv_dtype target_dtype,
+    const void *draft_logits, sv_dtype draft_dtype,
+    const int32_t *draft_tokens, const int32_t *d2t,
+    const float *u_accept, const float *u_sample,
+    int32_t B, int32_t gamma, int32_t Vt, int32_t Vd,
+    float temperature, float top_p,
+    int32_t *out_tokens, int32_t *out_accept_len,
+    float *out_p_tok, float *out_q_tok, int32_t *out_status,
+    hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char *spec_verify_strerror(sv_status s);
 
