@@ -51,7 +51,9 @@ def _load():
         i32, f64 = C.c_int, C.c_double
         lib.oracle_verify_sample.argtypes = [P, i32, P, i32, P, P, P, P, i32, i32, i32, i32,
                                              f64, f64, f64, P, P, P, P, P, P, P, P, i32]
-        lib.oracle_row_dist.argtypes = [P, i32, i32, f64, f64, i32, P, P, P, P]
+        lib.oracle_row_dist.argtypes = [P, i32, i32, f64, f64, i32, i32, P, P, P, P]
+        lib.oracle_draft_sample.argtypes = [P, i32, P, P, i32, i32, f64, f64, i32, f64, P, P, P, P, P, P, P]
+        lib.oracle_count.argtypes = [P, i32, i32, P]
         lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, C.c_double, P, P]
         lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
         lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
@@ -107,15 +109,17 @@ def verify_sample(target_logits, draft_logits, tokens, u_accept, u_sample, tempe
     return out
 
 
-def row_dist(z, temperature, top_p, k_delta=0):
-    """D1 on one row: returns (p [V] float64, status, k, margin_lo, margin_hi)."""
+def row_dist(z, temperature, top_p, k_delta=0, top_k=0):
+    """D1 on one row: returns (p [V] float64, status, k, margin_lo, margin_hi).
+    top_k caps the kept count (the draft-side sampler's reading; 0 = off); k
+    is the top-p count before the cap."""
     z, dt = _logits(np.asarray(z).reshape(-1))
     V = z.shape[0]
     p = np.empty(V, np.float64)
     k = np.zeros(1, np.int32)
     lo = np.zeros(1, np.float64)
     hi = np.zeros(1, np.float64)
-    st = _load().oracle_row_dist(_ptr(z), dt, V, float(temperature), float(top_p), int(k_delta),
+    st = _load().oracle_row_dist(_ptr(z), dt, V, float(temperature), float(top_p), int(top_k), int(k_delta),
                                  _ptr(p), _ptr(k), _ptr(lo), _ptr(hi))
     if st < 0:
         raise ValueError("oracle_row_dist: bad arguments")
@@ -143,6 +147,37 @@ def chain_from_dists(P, Q, tokens, u_accept, u_sample, band=0.0):
     if n < 0:
         raise MemoryError("oracle_chain_from_dists")
     return n, out, int(fl[0])
+
+
+def draft_sample(logits, u, temperature, top_p, top_k=0, d2t=None, band=1e-5, k_delta=None):
+    """D9: one draw per row of logits [B, V] with uniforms u [B].  Returns a
+    dict: tokens [B] (target ids through d2t when given), prob [B] (p of the
+    drawn id, float64), status [B], flags [B] (CDF-edge diagnostics), margin
+    [B, 2] (top-p margins), k [B] (top-p count before the top-k cap)."""
+    lg, dt = _logits(logits)
+    B, V = lg.shape
+    uu = np.ascontiguousarray(u, dtype=np.float32).reshape(B)
+    dm = None if d2t is None else np.ascontiguousarray(d2t, dtype=np.int32)
+    kd = None if k_delta is None else np.ascontiguousarray(k_delta, dtype=np.int8).reshape(B)
+    out = dict(tokens=np.empty(B, np.int32), prob=np.empty(B, np.float64), status=np.empty(B, np.int32),
+               flags=np.empty(B, np.int32), margin=np.empty((B, 2), np.float64), k=np.empty(B, np.int32))
+    rc = _load().oracle_draft_sample(_ptr(lg), dt, _ptr(dm), _ptr(uu), B, V, float(temperature), float(top_p),
+                                     int(top_k), float(band), _ptr(kd), _ptr(out["tokens"]), _ptr(out["prob"]),
+                                     _ptr(out["status"]), _ptr(out["flags"]), _ptr(out["margin"]), _ptr(out["k"]))
+    if rc != 0:
+        raise ValueError("oracle_draft_sample: bad arguments (code %d)" % rc)
+    return out
+
+
+def count(accept_len, gamma, counters=None):
+    """Acceptance counters (target calls, drafted, accepted, emitted, invalid)
+    after adding one call's accept_len [B]."""
+    a = np.ascontiguousarray(accept_len, dtype=np.int32).reshape(-1)
+    c = np.zeros(5, np.uint64) if counters is None else np.ascontiguousarray(counters, dtype=np.uint64).copy()
+    rc = _load().oracle_count(_ptr(a), a.shape[0], int(gamma), _ptr(c))
+    if rc != 0:
+        raise ValueError("oracle_count: bad arguments")
+    return c
 
 
 def verify_greedy(logits, tokens):

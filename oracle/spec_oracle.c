@@ -97,10 +97,15 @@ typedef struct {
  *   3. p = softmax over the kept logits (removed ones are -inf).
  * k_delta (tests only) moves the kept count to k + k_delta, to enumerate the
  * admissible alternatives when cum_incl lands within a rounding band of rho.
+ * top_k (the draft-side sampler; 0 elsewhere): [Ling tutorial] sec. 3.1 names
+ * top-k beside top-p for drawing draft tokens and gives no rule for combining
+ * them.  Read plainly, both filters cut the same stable order of step 2: top-k
+ * keeps its first top_k positions, top-p its first k, so together they keep
+ * the first min(top_k, k) positions.  top_k <= 0 or >= V is off.
  * Returns 0, or ORC_ST_NO_MASS when max y is not finite (p is then all zero).
  */
 static int row_dist(const void *base, int dtype, size_t off, int V, double T,
-                    double rho, int k_delta, double *p, yid_t *scratch,
+                    double rho, int top_k, int k_delta, double *p, yid_t *scratch,
                     topp_info_t *info)
 {
     int j;
@@ -116,8 +121,9 @@ static int row_dist(const void *base, int dtype, size_t off, int V, double T,
         for (j = 0; j < V; ++j) p[j] = 0.0;
         return ORC_ST_NO_MASS;
     }
+    const int topk_on = top_k > 0 && top_k < V;
 
-    if (rho < 1.0) {
+    if (rho < 1.0 || topk_on) {
         /* softmax over all V, sum in id order */
         double Z = 0.0;
         for (j = 0; j < V; ++j) Z += exp(p[j] - m);
@@ -130,7 +136,7 @@ static int row_dist(const void *base, int dtype, size_t off, int V, double T,
          * predecessor's inclusive cum exceeds rho */
         int k = V;
         double cum = 0.0, cum_prev_prev = 0.0;
-        for (int s = 0; s < V; ++s) {
+        for (int s = 0; s < V && rho < 1.0; ++s) {
             double pi = exp(scratch[s].y - m) / Z;
             cum_prev_prev = cum;          /* cum_incl(s-1) */
             cum += pi;                    /* cum_incl(s)   */
@@ -141,7 +147,7 @@ static int row_dist(const void *base, int dtype, size_t off, int V, double T,
                 break;
             }
         }
-        if (k == V && V >= 2) {
+        if (k == V && V >= 2 && rho < 1.0) {
             /* everything kept: the last kept position's predecessor margin */
             double c = 0.0;
             for (int s = 0; s < V - 1; ++s) c += exp(scratch[s].y - m) / Z;
@@ -151,6 +157,7 @@ static int row_dist(const void *base, int dtype, size_t off, int V, double T,
         int kk = k + k_delta;
         if (kk < 1) kk = 1;
         if (kk > V) kk = V;
+        if (topk_on && kk > top_k) kk = top_k;       /* top-k cuts the same order */
         /* removed ids become -inf, as the page's filter writes them */
         for (int s = kk; s < V; ++s) p[scratch[s].id] = -INFINITY;
     }
@@ -241,7 +248,7 @@ static void verify_sample_seq(sample_job_t *J, int b, double *P, double *Q,
         topp_info_t info;
         int kd = J->k_delta ? J->k_delta[(size_t)b * nrows + i] : 0;
         size_t off = ((size_t)b * (g + 1) + i) * (size_t)Vt;
-        status |= row_dist(J->tl, J->tdt, off, Vt, J->T, J->rho, kd, P + (size_t)i * Vt, scr, &info);
+        status |= row_dist(J->tl, J->tdt, off, Vt, J->T, J->rho, 0, kd, P + (size_t)i * Vt, scr, &info);
         if (J->out_margin) {
             J->out_margin[((size_t)b * nrows + i) * 2 + 0] = info.margin_lo;
             J->out_margin[((size_t)b * nrows + i) * 2 + 1] = info.margin_hi;
@@ -253,12 +260,12 @@ static void verify_sample_seq(sample_job_t *J, int b, double *P, double *Q,
         size_t off = ((size_t)b * g + i) * (size_t)Vd;
         double *q = Q + (size_t)i * Vt;
         if (J->d2t == NULL) {
-            status |= row_dist(J->dl, J->ddt, off, Vd, J->T, J->rho, kd, q, scr, &info);
+            status |= row_dist(J->dl, J->ddt, off, Vd, J->T, J->rho, 0, kd, q, scr, &info);
         } else {
             /* [SSD guide] sec. 6: the draft head covers a reduced vocabulary and
              * d2t scatters it into the target vocabulary; ids off the map get
              * probability 0. */
-            status |= row_dist(J->dl, J->ddt, off, Vd, J->T, J->rho, kd, qc, scr, &info);
+            status |= row_dist(J->dl, J->ddt, off, Vd, J->T, J->rho, 0, kd, qc, scr, &info);
             for (int t = 0; t < Vt; ++t) q[t] = 0.0;
             for (int jd = 0; jd < Vd; ++jd) q[J->d2t[jd]] = qc[jd];
         }
@@ -429,17 +436,19 @@ int oracle_verify_sample(const void *tl, int tdt, const void *dl, int ddt,
 }
 
 /*
- * One row's distribution, exposed for the pins: p [V] receives D1's output.
- * Returns the status bits; *k, *margin_lo, *margin_hi as in topp_info_t.
+ * One row's distribution, exposed for the pins: p [V] receives D1's output
+ * (with the top_k cap of the draft-side sampler; 0 = off).
+ * Returns the status bits; *k, *margin_lo, *margin_hi as in topp_info_t
+ * (k is the top-p count before the top-k cap).
  */
-int oracle_row_dist(const void *z, int dtype, int V, double T, double rho, int k_delta,
+int oracle_row_dist(const void *z, int dtype, int V, double T, double rho, int top_k, int k_delta,
                     double *p, int32_t *k, double *margin_lo, double *margin_hi)
 {
     if (V < 1 || !(T > 0.0) || !(rho > 0.0)) return -ORC_EARG;
     yid_t *scr = malloc(sizeof(yid_t) * (size_t)V);
     if (!scr) return -ORC_EMEM;
     topp_info_t info;
-    int st = row_dist(z, dtype, 0, V, T, rho, k_delta, p, scr, &info);
+    int st = row_dist(z, dtype, 0, V, T, rho, top_k, k_delta, p, scr, &info);
     free(scr);
     if (k) *k = info.k;
     if (margin_lo) *margin_lo = info.margin_lo;
@@ -497,6 +506,76 @@ int oracle_chain_from_dists(const double *P, const double *Q, const int32_t *tok
     out_tokens[n] = pick;
     if (out_flags) *out_flags = flags;
     return n;
+}
+
+/* ------------------------------------------------------------------------- */
+/* D9: the draft-side sampler and the acceptance counters.                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * One draft token per row, [Ling tutorial] sec. 4.2 (the draft loop of
+ * generate(): logits / temperature, _apply_top_p, F.softmax,
+ * torch.multinomial) and sec. 3.1 (drafting by argmax or top-p/top-k):
+ *   p = row_dist(z / T, top-p rho, top-k cap) as in D1 with the top_k reading
+ *   above; the token is the inverse-CDF draw of D4 with the caller's uniform
+ *   u[b] (ascending id, strict >).  With d2t (a reduced draft vocabulary,
+ *   [SSD guide] sec. 6) the drawn draft id j is reported as target id d2t[j].
+ * logits [B, V]; u [B]; out_tokens [B]; out_prob [B] = p of the drawn id;
+ * out_status [B] (ORC_ST_NO_MASS; may be NULL); out_flags [B] (ORC_FL_CDF_EDGE
+ * when u is within band of an interior edge; may be NULL); out_margin [B, 2]
+ * top-p margins and out_k [B] the top-p count before the top-k cap (may be
+ * NULL); k_delta [B] or NULL moves the top-p count (tests only).
+ */
+int oracle_draft_sample(const void *logits, int dtype, const int32_t *d2t, const float *u,
+                        int B, int V, double T, double rho, int top_k, double band,
+                        const int8_t *k_delta, int32_t *out_tokens, double *out_prob,
+                        int32_t *out_status, int32_t *out_flags, double *out_margin,
+                        int32_t *out_k)
+{
+    if (B < 0 || V < 1 || !(T > 0.0) || !(rho > 0.0)) return ORC_EARG;
+    double *p = malloc(sizeof(double) * (size_t)V);
+    yid_t *scr = malloc(sizeof(yid_t) * (size_t)V);
+    if (!p || !scr) { free(p); free(scr); return ORC_EMEM; }
+    for (int b = 0; b < B; ++b) {
+        topp_info_t info;
+        int kd = k_delta ? k_delta[b] : 0;
+        int st = row_dist(logits, dtype, (size_t)b * (size_t)V, V, T, rho, top_k, kd, p, scr, &info);
+        int edge = 0;
+        int32_t pick = st ? -1 : inverse_cdf(p, V, (double)u[b], band, &edge);
+        out_tokens[b] = (pick >= 0 && d2t) ? d2t[pick] : pick;
+        out_prob[b] = pick >= 0 ? p[pick] : 0.0;
+        if (out_status) out_status[b] = st;
+        if (out_flags) out_flags[b] = edge ? ORC_FL_CDF_EDGE : 0;
+        if (out_margin) { out_margin[2 * b] = info.margin_lo; out_margin[2 * b + 1] = info.margin_hi; }
+        if (out_k) out_k[b] = info.k;
+    }
+    free(p); free(scr);
+    return ORC_OK;
+}
+
+/*
+ * Acceptance counters over one verification call, [Ling tutorial] sec. 4.2
+ * (the statistics of generate(): total_tokens, total_target_calls,
+ * total_draft_calls, avg_acceptance_rate = sum of accepted counts /
+ * (rounds * draft_length), speedup_estimate = tokens / target calls):
+ *   counters[0] += B            target calls (one verification pass per sequence)
+ *   counters[1] += B * gamma    draft tokens proposed (gamma draft calls each)
+ *   counters[2] += sum n_b      draft tokens accepted
+ *   counters[3] += sum (n_b+1)  tokens emitted (accepted drafts plus the drawn one)
+ *   counters[4] += #{b : n_b outside [0, gamma]}  (such entries add to no other counter)
+ */
+int oracle_count(const int32_t *accept_len, int B, int gamma, uint64_t *counters)
+{
+    if (B < 0 || gamma < 0) return ORC_EARG;
+    for (int b = 0; b < B; ++b) {
+        int32_t n = accept_len[b];
+        if (n < 0 || n > gamma) { counters[4] += 1; continue; }
+        counters[0] += 1;
+        counters[1] += (uint64_t)gamma;
+        counters[2] += (uint64_t)n;
+        counters[3] += (uint64_t)n + 1;
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------------- */
