@@ -22,7 +22,8 @@ Prints ONE JSON line: verified vocab rows/s (target + draft rows per second),
 the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
 launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
 the same workload (one thread and every host core).  The default run then
-times the other four workloads the same way and reports each under
+times the other workloads the same way (the four other verification
+configurations and the draft-side sampler) and reports each under
 config.workloads (step time, rows/s, GB/s and fraction of peak, counter
 traffic, the oracle's rows/s).
 """
@@ -50,11 +51,15 @@ WORKLOADS = {
     "greedy": dict(desc="greedy verify, B=128 gamma=6 V=128256 bf16"),
     "eagle_d2t": dict(desc="EAGLE3 d2t sampling verify, B=32 gamma=7 Vt=128256 bf16 Vd=32000 fp32, T=1"),
     "tree": dict(desc="greedy tree verify, B=16 N=32 V=49152 bf16"),
+    "draft": dict(desc="draft-side sampler, B=64 V=151936 bf16, T=0.8 top_p=0.9 top_k=50"),
 }
 
 
 def compulsory_bytes(w) -> int:
     """Every input byte read once plus every output byte written once."""
+    if w["kind"] == "draft":
+        B = w["logits"].shape[0]
+        return int(w["logits"].nbytes + w["u"].nbytes + 3 * B * 4)       # logits, uniforms; token, prob, status
     n = w["target"].nbytes + w["tokens"].nbytes
     if w["kind"] == "sample":
         n += w["draft"].nbytes + w["u_accept"].nbytes + w["u_sample"].nbytes
@@ -72,6 +77,8 @@ def compulsory_bytes(w) -> int:
 
 
 def rows_per_step(w) -> int:
+    if w["kind"] == "draft":
+        return int(w["logits"].shape[0])
     if w["kind"] == "sample":
         B, g = w["tokens"].shape
         return B * (2 * g + 1)
@@ -96,6 +103,11 @@ def device_sets(w, nrot, dev):
             return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a.copy()).to(dev)
 
+    if w["kind"] == "draft":
+        base = dict(logits=t(w["logits"]), u=t(w["u"]))
+        sets = [base] + [dict(base, logits=base["logits"].clone()) for _ in range(nrot - 1)]
+        torch.cuda.synchronize()
+        return sets
     base = dict(target=t(w["target"]), tokens=t(w["tokens"].astype(np.int32)))
     if w["kind"] == "sample":
         base.update(draft=t(w["draft"]), u_accept=t(w["u_accept"]), u_sample=t(w["u_sample"]),
@@ -130,11 +142,14 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float, threads: int):
     time x threads used) have been spent."""
     import oracle
     oracle.build(force=False)
-    B = w["target"].shape[0]
+    B = (w["logits"] if w["kind"] == "draft" else w["target"]).shape[0]
     s = min(B, max_seqs)
     sl = slice(0, s)
 
     def one_pass():
+        if w["kind"] == "draft":
+            oracle.draft_sample(w["logits"][sl], w["u"][sl], w["temperature"], w["top_p"], top_k=w["top_k"])
+            return s, 1
         if w["kind"] == "sample":
             oracle.verify_sample(w["target"][sl], w["draft"][sl], w["tokens"][sl], w["u_accept"][sl],
                                  w["u_sample"][sl], w["temperature"], w["top_p"], d2t=w.get("d2t"),
@@ -164,7 +179,7 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
     ncores = min(len(os.sched_getaffinity(0)), 64)
     one = cpu_baseline(w, max(1, max_seqs // 8), work_seconds, 1)
     many = cpu_baseline(w, max_seqs, work_seconds, ncores) if w["kind"] == "sample" and ncores > 1 else one
-    B = w["target"].shape[0]
+    B = (w["logits"] if w["kind"] == "draft" else w["target"]).shape[0]
     return dict(value=many["value"], unit="rows/s", cores=many["cores"], kind="oracle",
                 value_1thread=one["value"], cores_available=ncores, nproc=os.cpu_count(), cpu_model=cpu_model(),
                 sample="1 thread: %d pass(es) over the first %d of %d sequences, %.2f s wall; "
@@ -175,7 +190,7 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
 
 KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
-               tree="greedy_kernel+seq_kernel")
+               tree="greedy_kernel+seq_kernel", draft="draft_kernel")
 
 
 def measure(name, args, dev, log):
@@ -192,7 +207,15 @@ def measure(name, args, dev, log):
     stream = torch.cuda.current_stream(dev)
 
     # preallocated outputs and one workspace (calls on one stream share it)
-    if w["kind"] == "sample":
+    if w["kind"] == "draft":
+        B, V = w["logits"].shape
+        need = sv.sv_workspace_bytes_draft(B, V)
+        outs = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.float32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+
+        def step(s):
+            sv.spec_draft_sample(s["logits"], s["u"], w["temperature"], w["top_p"], w["top_k"], ws=ws, out=outs)
+    elif w["kind"] == "sample":
         B, g = w["tokens"].shape
         Vt = w["target"].shape[2]
         Vd = w["draft"].shape[2]
@@ -265,10 +288,11 @@ def measure(name, args, dev, log):
     # launch-to-launch duration (for the multi-kernel paths, of the call).
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     res = dict(workload=name, desc=WORKLOADS[name]["desc"], kernel=KERNELS[name],
-               logits_dtype=str(w["target"].dtype).replace("uint16", "bf16"),
+               logits_dtype=str((w["logits"] if w["kind"] == "draft" else w["target"]).dtype).replace("uint16", "bf16"),
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
                ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
-               seqs_per_s=float(w["target"].shape[0] * K / (total_ms / 1e3)),
+               seqs_per_s=float((w["logits"] if w["kind"] == "draft" else w["target"]).shape[0] * K
+                                / (total_ms / 1e3)),
                achieved_GBps=achieved, frac=achieved / PEAK_GBS,
                traffic=read_traffic(args.traffic_table, name),
                launch_ms_mean=float(np.mean(per_launch_ms)), launch_ms_median=float(np.median(per_launch_ms)),
@@ -332,8 +356,8 @@ def main():
         print(msg, file=sys.stderr, flush=True)
 
     head = args.workload
-    names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp")
-                                            if n != head])
+    names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp",
+                                                         "draft") if n != head])
     results, inputs = {}, {}
     for name in names:
         inputs[name], results[name] = measure(name, args, dev, log)

@@ -10,6 +10,8 @@ calling any entry point without it raises.
         temperature, top_p, d2t=None)
     tokens, accept_len, p_tok, q_tok, status = spec_verify_sample_noalloc(..., out=outputs)
     tokens, accept_len, status = spec_verify_greedy(target_logits, draft_tokens)
+    tokens, prob, status = spec_draft_sample(logits, u, temperature, top_p, top_k)
+    spec_verify_count(accept_len, gamma, counters)
     path, tokens, accept_len, status = spec_verify_tree_greedy(target_logits, node_tokens, parents)
 
 Tensors must live on the same GPU and be contiguous: logits float32 or
@@ -76,6 +78,13 @@ def lib() -> C.CDLL:
                 L.spec_verify_sample_noalloc.restype = C.c_int
                 L.spec_verify_sample_noalloc.argtypes = [P, C.c_int, P, C.c_int, P, P, P, P, i32, i32, i32, i32,
                                                          C.c_float, C.c_float, P, P, P, P, P, P]
+                L.sv_workspace_bytes_draft.restype = sz
+                L.sv_workspace_bytes_draft.argtypes = [i32, i32]
+                L.spec_draft_sample.restype = C.c_int
+                L.spec_draft_sample.argtypes = [P, C.c_int, P, P, i32, i32, C.c_float, C.c_float, i32,
+                                                P, P, P, P, sz, P]
+                L.spec_verify_count.restype = C.c_int
+                L.spec_verify_count.argtypes = [P, i32, i32, P, P]
                 L.spec_verify_tree_greedy.restype = C.c_int
                 L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
                 _lib = L
@@ -234,6 +243,48 @@ def spec_verify_sample_noalloc(target_logits, draft_logits, draft_tokens, u_acce
         _ptr(out_tokens), _ptr(out_len), _ptr(out_p), _ptr(out_q), _ptr(out_status), _stream(dev))
     _raise("spec_verify_sample_noalloc", rc)
     return out_tokens, out_len, out_p, out_q, out_status
+
+
+def sv_workspace_bytes_draft(B, V) -> int:
+    return int(lib().sv_workspace_bytes_draft(B, V))
+
+
+def spec_draft_sample(logits, u, temperature: float, top_p: float = 1.0, top_k: int = 0, d2t=None, *,
+                      ws: torch.Tensor | None = None, out=None):
+    """Draft-side sampler: one token per row of logits [B, V].  Returns
+    (tokens [B] int32, prob [B] float32, status [B] int32) device tensors."""
+    L = lib()
+    dev = logits.device
+    if logits.dim() != 2:
+        raise ValueError("logits must be [B, V]")
+    B, V = logits.shape
+    _check(logits, "logits", dev)
+    dt = _dtype_code(logits)
+    _check(u, "u", dev, torch.float32, (B,))
+    if d2t is not None:
+        _check(d2t, "d2t", dev, torch.int32, (V,))
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.float32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    need = sv_workspace_bytes_draft(B, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_draft_sample(_ptr(logits), dt, _ptr(d2t), _ptr(u), B, V, float(temperature), float(top_p), int(top_k),
+                             _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws), ws.numel(), _stream(dev))
+    _raise("spec_draft_sample", rc)
+    return out
+
+
+def spec_verify_count(accept_len, gamma: int, counters):
+    """Add one verification call's accept_len [B] to counters [5] (int64 device
+    tensor: target calls, drafts proposed, accepted, emitted, invalid)."""
+    L = lib()
+    dev = accept_len.device
+    _check(accept_len, "accept_len", dev, torch.int32)
+    _check(counters, "counters", dev, torch.int64, (5,))
+    rc = L.spec_verify_count(_ptr(accept_len), accept_len.numel(), int(gamma), _ptr(counters), _stream(dev))
+    _raise("spec_verify_count", rc)
+    return counters
 
 
 def spec_verify_greedy(target_logits, draft_tokens, *, ws: torch.Tensor | None = None, out=None):

@@ -244,6 +244,66 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+size_t sv_workspace_bytes_draft(int32_t B, int32_t V) {
+    if (B < 0 || V < 1 || V > SV_MAX_VOCAB) return 0;
+    DraftLayout L;
+    int32_t C;
+    draft_layout(B, V, &L, &C);
+    return workspace_need(L.counter_bytes, L.data_bytes);
+}
+
+sv_status spec_draft_sample(const void *logits, sv_dtype dtype, const int32_t *d2t, const float *u, int32_t B,
+                            int32_t V, float temperature, float top_p, int32_t top_k, int32_t *out_tokens,
+                            float *out_prob, int32_t *out_status, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+    if (B < 0 || V < 1) return SV_ERR_INVALID_ARG;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
+    if (!(top_p > 0.0f)) return SV_ERR_INVALID_ARG;
+    if (V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!logits || !u || !out_tokens || !workspace) return SV_ERR_INVALID_ARG;
+    if (!aligned(logits, esize(dtype))) return SV_ERR_INVALID_ARG;
+    DraftLayout L;
+    int32_t C;
+    draft_layout(B, V, &L, &C);
+    if (!workspace_fits(workspace_bytes, L.counter_bytes, L.data_bytes)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (!grid_fits((int64_t)B * C)) return SV_ERR_TOO_LARGE;
+    DraftArgs a;
+    a.logits = logits;
+    a.d2t = d2t;
+    a.u = u;
+    a.B = B;
+    a.V = V;
+    a.C = C;
+    a.T = temperature;
+    a.c = 1.4426950408889634f / temperature;
+    a.top_p = top_p;
+    a.top_k = (top_k > 0 && top_k < V) ? top_k : 0;
+    a.out_tokens = out_tokens;
+    a.out_prob = out_prob;
+    a.out_status = out_status;
+    char *base = static_cast<char *>(workspace);
+    char *data = base + counter_region(workspace_bytes);
+    a.counters = reinterpret_cast<uint32_t *>(base);
+    a.res = reinterpret_cast<ChunkRes *>(data + L.res);
+    a.cand = reinterpret_cast<uint64_t *>(data + L.cand);
+    a.desc = reinterpret_cast<RowDesc *>(data + L.desc);
+    return launch_draft(a, dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma, uint64_t *counters,
+                            hipStream_t stream) {
+    if (B < 0 || gamma < 0) return SV_ERR_INVALID_ARG;
+    if (gamma > SV_MAX_GAMMA) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!accept_len || !counters) return SV_ERR_INVALID_ARG;
+    if (!aligned(counters, sizeof(uint64_t))) return SV_ERR_INVALID_ARG;
+    return launch_count(accept_len, B, gamma, reinterpret_cast<unsigned long long *>(counters), stream) == hipSuccess
+               ? SV_OK
+               : SV_ERR_HIP;
+}
+
 sv_status spec_verify_sample_noalloc(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
                                      sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
                                      const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,

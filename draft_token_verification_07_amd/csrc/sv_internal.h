@@ -178,6 +178,41 @@ struct SampleArgs {
     int32_t *tile_jb;          // [ntiles + 1] first draft id of each draw tile under d2t (plain mode)
 };
 
+// ---------------------------------------------------------------------------
+// Draft-side sampler
+// ---------------------------------------------------------------------------
+struct ChunkRes {     // one chunk of a draft row: online (max, sum) and its band
+    float m, s;
+    int32_t n;        // band tokens published (<= kCandCap), -1 when the band overflowed
+    int32_t pad;
+};
+
+struct DraftArgs {
+    const void *logits;        // [B, V]
+    const int32_t *d2t;        // [V] or null: report target id d2t[j] for draft id j
+    const float *u;            // [B]
+    int32_t B, V, C;           // C chunks per row
+    float T, c, top_p;         // c = log2(e) / T
+    int32_t top_k;             // 0 = off
+    int32_t *out_tokens;
+    float *out_prob;
+    int32_t *out_status;
+    // workspace
+    uint32_t *counters;        // [B] arrivals
+    ChunkRes *res;             // [B, C]
+    uint64_t *cand;            // [B, C, kCandCap] ordering codes of band tokens
+    RowDesc *desc;             // [B] (exact fallback)
+};
+struct DraftLayout {
+    size_t counter_bytes;
+    size_t res, cand, desc, data_bytes;   // offsets from K
+};
+int32_t draft_chunks(int32_t B, int32_t V);
+void draft_layout(int32_t B, int32_t V, DraftLayout *L, int32_t *C);
+hipError_t launch_draft(const DraftArgs &a, int dtype, hipStream_t st);
+hipError_t launch_count(const int32_t *accept_len, int32_t B, int32_t gamma, unsigned long long *counters,
+                        hipStream_t st);
+
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,
 // with K = counter_region(W) -- a function of W alone.  Every call returns
 // its counters to zero, and no call ever writes data below K, so calls of any

@@ -29,6 +29,8 @@ Workloads (sizes are parameters; the defaults are the full sizes):
   tree           B=16, N=32 nodes, depth <= 5, <= 8 children, V=49152, bf16 ~N(0, 2^2);
                  node token = argmax of its parent's row with probability 0.6 (the 2.16x
                  blog's 32-node, depth-5, top-k-8 tree).
+  draft          B=64 rows, V=151936, bf16, shaped like sample_topp's rows; T=0.8,
+                 top-p 0.9, top-k 50 (the draft-side sampler).
 """
 from __future__ import annotations
 
@@ -136,6 +138,19 @@ def eagle_d2t(seed: int, B: int = 32, gamma: int = 7, Vt: int = 128256, Vd: int 
                 u_sample=uniforms(rng, (B,)), d2t=d2t, temperature=temperature, top_p=1.0)
 
 
+def draft(seed: int, B: int = 64, V: int = 151936, spike_frac: float = 0.01, temperature: float = 0.8,
+          top_p: float = 0.9, top_k: int = 50, bf16: bool = True) -> dict:
+    """Draft-side sampler input: B rows shaped like the sampling workload's
+    (N(0, 3^2), 1% of the ids of every row raised by +8), one uniform per row."""
+    rng = np.random.default_rng(seed)
+    z = _normal(rng, (B, V), 3.0)
+    n_spike = max(1, int(round(spike_frac * V)))
+    for b in range(B):
+        z[b, rng.choice(V, n_spike, replace=False)] += np.float32(8.0)
+    return dict(kind="draft", logits=bf16_bits(z) if bf16 else z, u=uniforms(rng, (B,)),
+                temperature=temperature, top_p=top_p, top_k=top_k, d2t=None)
+
+
 def tree_topology(rng: np.random.Generator, N: int = 32, max_depth: int = 5, max_children: int = 8):
     """Random parent array: node 0 is the root; node k picks a parent uniformly
     among earlier nodes with depth < max_depth and fewer than max_children children."""
@@ -171,4 +186,5 @@ WORKLOADS = {
     "greedy": greedy,
     "eagle_d2t": eagle_d2t,
     "tree": tree,
+    "draft": draft,
 }

@@ -190,6 +190,61 @@ sv_status spec_verify_tree_greedy(
     int32_t *out_status, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Draft-side sampler ("Ling-3.0-flash-dspark" tutorial sec. 4.2: the draft
+ * loop of generate() -- logits / temperature, _apply_top_p, softmax,
+ * multinomial; sec. 3.1: draft tokens by argmax or top-p/top-k).  One token
+ * per row: p = softmax(logits[b] / temperature) over the first
+ * min(top_k, k_p) positions of the stable order (logit descending, lower id
+ * first), where k_p is the top-p count of spec_verify_sample's rule (top-p
+ * and top-k cut the same order; the pages give no other rule for combining
+ * them).  The token is the inverse-CDF draw in ascending id with u[b], the
+ * rule of spec_verify_sample's draws.
+ *   logits      [B, V] of dtype (row-major, any row alignment).
+ *   d2t         [V] int32 or NULL: report draft id j as target id d2t[j]
+ *               (SSD guide sec. 6); the entry is reported as it is.
+ *   u           [B] float32 in [0, 1).
+ *   temperature > 0 and finite.  top_p in (0, 1), >= 1 = off.
+ *   top_k       <= 0 or >= V = off.
+ *   out_tokens  [B] int32: the drawn id (through d2t), -1 for a row whose
+ *               maximum is not finite.
+ *   out_prob    [B] float32 or NULL: p of the drawn id (the draft
+ *               probability q(x) that verification compares with).
+ *   out_status  [B] int32 or NULL: SV_SEQ_NO_MASS.
+ *   workspace   >= sv_workspace_bytes_draft(B, V) bytes, zeroed once when
+ *               allocated, as for the other entry points.
+ * Errors: SV_ERR_INVALID_ARG (null required pointer, B < 0, V < 1, a bad
+ * temperature or top_p), SV_ERR_UNSUPPORTED_DTYPE, SV_ERR_TOO_LARGE
+ * (V > SV_MAX_VOCAB), SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP.
+ */
+size_t sv_workspace_bytes_draft(int32_t B, int32_t V);
+sv_status spec_draft_sample(
+    const void *logits, sv_dtype dtype, const int32_t *d2t, const float *u,
+    int32_t B, int32_t V, float temperature, float top_p, int32_t top_k,
+    int32_t *out_tokens, float *out_prob, int32_t *out_status,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Acceptance counters ("Ling-3.0-flash-dspark" tutorial sec. 4.2: the
+ * statistics generate() returns -- total tokens, target calls, draft calls,
+ * avg_acceptance_rate = accepted / (rounds * draft_length) and
+ * speedup_estimate = tokens / target calls).  Adds one verification call's
+ * out_accept_len [B] (draft length gamma) to counters [5] uint64 (device
+ * memory, zeroed by the caller before the first call):
+ *   counters[0] += target calls (one per sequence),
+ *   counters[1] += drafts proposed (gamma per sequence),
+ *   counters[2] += drafts accepted (sum of accept_len),
+ *   counters[3] += tokens emitted (accept_len + 1 per sequence),
+ *   counters[4] += entries outside [0, gamma] (which add to no other counter).
+ * Acceptance rate = counters[2] / counters[1]; tokens per target call =
+ * counters[3] / counters[0].  Integer sums: exact in any order.  Calls on
+ * several streams may share counters (64-bit atomic adds).
+ * Errors: SV_ERR_INVALID_ARG (B < 0, gamma < 0, null pointers, counters not
+ * 8-byte aligned), SV_ERR_TOO_LARGE (gamma > SV_MAX_GAMMA), SV_ERR_HIP.
+ */
+sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma, uint64_t *counters,
+                            hipStream_t stream);
+
+/*
  * Sampling verification without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs and results are those
