@@ -23,7 +23,7 @@ the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
 launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
 the same workload (one thread and every host core).  The default run then
 times the other workloads the same way (the four other verification
-configurations and the draft-side sampler) and reports each under
+configurations, the draft-side sampler and the SSD fan-out lookup) and reports each under
 config.workloads (step time, rows/s, GB/s and fraction of peak, counter
 traffic, the oracle's rows/s).
 """
@@ -52,6 +52,7 @@ WORKLOADS = {
     "eagle_d2t": dict(desc="EAGLE3 d2t sampling verify, B=32 gamma=7 Vt=128256 bf16 Vd=32000 fp32, T=1"),
     "tree": dict(desc="greedy tree verify, B=16 N=32 V=49152 bf16"),
     "draft": dict(desc="draft-side sampler, B=64 V=151936 bf16, T=0.8 top_p=0.9 top_k=50"),
+    "fanout": dict(desc="SSD fan-out lookup, B=64 gamma=7 f=3 L=8"),
 }
 
 
@@ -60,6 +61,11 @@ def compulsory_bytes(w) -> int:
     if w["kind"] == "draft":
         B = w["logits"].shape[0]
         return int(w["logits"].nbytes + w["u"].nbytes + 3 * B * 4)       # logits, uniforms; token, prob, status
+    if w["kind"] == "fanout":
+        B, g1, f = w["cand"].shape
+        L = w["drafts"].shape[2]
+        # tokens at n, lengths, the f candidates at n, one branch's drafts read; branch and drafts written
+        return int(B * (4 + 4 + 4 * f + 4 * L) + B * (4 + 4 * L))
     n = w["target"].nbytes + w["tokens"].nbytes
     if w["kind"] == "sample":
         n += w["draft"].nbytes + w["u_accept"].nbytes + w["u_sample"].nbytes
@@ -77,6 +83,8 @@ def compulsory_bytes(w) -> int:
 
 
 def rows_per_step(w) -> int:
+    if w["kind"] == "fanout":
+        return int(w["cand"].shape[0])
     if w["kind"] == "draft":
         return int(w["logits"].shape[0])
     if w["kind"] == "sample":
@@ -103,6 +111,10 @@ def device_sets(w, nrot, dev):
             return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a.copy()).to(dev)
 
+    if w["kind"] == "fanout":
+        base = {k: t(w[k]) for k in ("out_tokens", "accept_len", "cand", "drafts")}
+        torch.cuda.synchronize()
+        return [base]
     if w["kind"] == "draft":
         base = dict(logits=t(w["logits"]), u=t(w["u"]))
         sets = [base] + [dict(base, logits=base["logits"].clone()) for _ in range(nrot - 1)]
@@ -125,6 +137,11 @@ def device_sets(w, nrot, dev):
     return sets
 
 
+def _batch(w) -> int:
+    key = {"draft": "logits", "fanout": "cand"}.get(w["kind"], "target")
+    return int(w[key].shape[0])
+
+
 def cpu_model() -> str:
     try:
         for ln in open("/proc/cpuinfo"):
@@ -142,11 +159,14 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float, threads: int):
     time x threads used) have been spent."""
     import oracle
     oracle.build(force=False)
-    B = (w["logits"] if w["kind"] == "draft" else w["target"]).shape[0]
+    B = _batch(w)
     s = min(B, max_seqs)
     sl = slice(0, s)
 
     def one_pass():
+        if w["kind"] == "fanout":
+            oracle.fanout_lookup(w["out_tokens"][sl], w["accept_len"][sl], w["cand"][sl], w["drafts"][sl])
+            return s, 1
         if w["kind"] == "draft":
             oracle.draft_sample(w["logits"][sl], w["u"][sl], w["temperature"], w["top_p"], top_k=w["top_k"])
             return s, 1
@@ -179,7 +199,7 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
     ncores = min(len(os.sched_getaffinity(0)), 64)
     one = cpu_baseline(w, max(1, max_seqs // 8), work_seconds, 1)
     many = cpu_baseline(w, max_seqs, work_seconds, ncores) if w["kind"] == "sample" and ncores > 1 else one
-    B = (w["logits"] if w["kind"] == "draft" else w["target"]).shape[0]
+    B = _batch(w)
     return dict(value=many["value"], unit="rows/s", cores=many["cores"], kind="oracle",
                 value_1thread=one["value"], cores_available=ncores, nproc=os.cpu_count(), cpu_model=cpu_model(),
                 sample="1 thread: %d pass(es) over the first %d of %d sequences, %.2f s wall; "
@@ -190,7 +210,7 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
 
 KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
-               tree="greedy_kernel+seq_kernel", draft="draft_kernel")
+               tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel")
 
 
 def measure(name, args, dev, log):
@@ -207,7 +227,14 @@ def measure(name, args, dev, log):
     stream = torch.cuda.current_stream(dev)
 
     # preallocated outputs and one workspace (calls on one stream share it)
-    if w["kind"] == "draft":
+    if w["kind"] == "fanout":
+        need = 256
+        ctr = torch.zeros(2, dtype=torch.int64, device=dev)
+
+        def step(s):
+            sv.spec_fanout_lookup(s["out_tokens"], s["accept_len"], s["cand"], s["drafts"], counters=ctr)
+        outs = None
+    elif w["kind"] == "draft":
         B, V = w["logits"].shape
         need = sv.sv_workspace_bytes_draft(B, V)
         outs = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.float32, device=dev),
@@ -288,11 +315,11 @@ def measure(name, args, dev, log):
     # launch-to-launch duration (for the multi-kernel paths, of the call).
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     res = dict(workload=name, desc=WORKLOADS[name]["desc"], kernel=KERNELS[name],
-               logits_dtype=str((w["logits"] if w["kind"] == "draft" else w["target"]).dtype).replace("uint16", "bf16"),
+               logits_dtype=("-" if w["kind"] == "fanout" else
+                             str((w["logits"] if w["kind"] == "draft" else w["target"]).dtype).replace("uint16", "bf16")),
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
                ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
-               seqs_per_s=float((w["logits"] if w["kind"] == "draft" else w["target"]).shape[0] * K
-                                / (total_ms / 1e3)),
+               seqs_per_s=float(_batch(w) * K / (total_ms / 1e3)),
                achieved_GBps=achieved, frac=achieved / PEAK_GBS,
                traffic=read_traffic(args.traffic_table, name),
                launch_ms_mean=float(np.mean(per_launch_ms)), launch_ms_median=float(np.median(per_launch_ms)),
@@ -357,7 +384,7 @@ def main():
 
     head = args.workload
     names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp",
-                                                         "draft") if n != head])
+                                                         "draft", "fanout") if n != head])
     results, inputs = {}, {}
     for name in names:
         inputs[name], results[name] = measure(name, args, dev, log)

@@ -85,6 +85,8 @@ def lib() -> C.CDLL:
                                                 P, P, P, P, sz, P]
                 L.spec_verify_count.restype = C.c_int
                 L.spec_verify_count.argtypes = [P, i32, i32, P, P]
+                L.spec_fanout_lookup.restype = C.c_int
+                L.spec_fanout_lookup.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P]
                 L.spec_verify_tree_greedy.restype = C.c_int
                 L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
                 _lib = L
@@ -285,6 +287,34 @@ def spec_verify_count(accept_len, gamma: int, counters):
     rc = L.spec_verify_count(_ptr(accept_len), accept_len.numel(), int(gamma), _ptr(counters), _stream(dev))
     _raise("spec_verify_count", rc)
     return counters
+
+
+def spec_fanout_lookup(out_tokens, accept_len, cand, branch_drafts=None, *, counters=None, want_next=True):
+    """SSD fan-out lookup.  cand [B, g+1, f], branch_drafts [B, (g+1) f, L].
+    Returns (branch [B] int32, next [B, L] int32 | None)."""
+    L_ = lib()
+    dev = out_tokens.device
+    B, g1 = out_tokens.shape
+    _check(out_tokens, "out_tokens", dev, torch.int32)
+    _check(accept_len, "accept_len", dev, torch.int32, (B,))
+    _check(cand, "cand", dev, torch.int32)
+    if cand.dim() != 3 or tuple(cand.shape[:2]) != (B, g1):
+        raise ValueError("cand must be [B, gamma+1, f]")
+    f = cand.shape[2]
+    Ln = 0
+    if branch_drafts is not None:
+        _check(branch_drafts, "branch_drafts", dev, torch.int32)
+        if branch_drafts.dim() != 3 or tuple(branch_drafts.shape[:2]) != (B, g1 * f):
+            raise ValueError("branch_drafts must be [B, (gamma+1) f, L]")
+        Ln = branch_drafts.shape[2]
+    if counters is not None:
+        _check(counters, "counters", dev, torch.int64, (2,))
+    br = torch.empty(B, dtype=torch.int32, device=dev)
+    nx = torch.empty((B, Ln), dtype=torch.int32, device=dev) if (want_next and branch_drafts is not None) else None
+    rc = L_.spec_fanout_lookup(_ptr(out_tokens), _ptr(accept_len), _ptr(cand), _ptr(branch_drafts), B, g1 - 1, f,
+                               Ln, _ptr(br), _ptr(nx), _ptr(counters), _stream(dev))
+    _raise("spec_fanout_lookup", rc)
+    return br, nx
 
 
 def spec_verify_greedy(target_logits, draft_tokens, *, ws: torch.Tensor | None = None, out=None):

@@ -304,6 +304,31 @@ sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma,
                : SV_ERR_HIP;
 }
 
+sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_len, const int32_t *cand,
+                             const int32_t *branch_drafts, int32_t B, int32_t gamma, int32_t f, int32_t L,
+                             int32_t *out_branch, int32_t *out_next, uint64_t *counters, hipStream_t stream) {
+    if (B < 0 || gamma < 0 || f < 1 || L < 0) return SV_ERR_INVALID_ARG;
+    if (gamma > SV_MAX_GAMMA || f > SV_MAX_FANOUT || L > SV_MAX_BRANCH_DRAFTS) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!out_tokens || !accept_len || !cand || !out_branch) return SV_ERR_INVALID_ARG;
+    if (out_next && L > 0 && !branch_drafts) return SV_ERR_INVALID_ARG;
+    if (counters && !aligned(counters, sizeof(uint64_t))) return SV_ERR_INVALID_ARG;
+    if (!grid_fits(((int64_t)B + 3) / 4)) return SV_ERR_TOO_LARGE;
+    FanoutArgs a;
+    a.out_tokens = out_tokens;
+    a.accept_len = accept_len;
+    a.cand = cand;
+    a.drafts = branch_drafts;
+    a.B = B;
+    a.gamma = gamma;
+    a.f = f;
+    a.L = L;
+    a.out_branch = out_branch;
+    a.out_next = (L > 0) ? out_next : nullptr;
+    a.counters = reinterpret_cast<unsigned long long *>(counters);
+    return launch_fanout(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 sv_status spec_verify_sample_noalloc(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
                                      sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
                                      const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,

@@ -213,6 +213,22 @@ hipError_t launch_draft(const DraftArgs &a, int dtype, hipStream_t st);
 hipError_t launch_count(const int32_t *accept_len, int32_t B, int32_t gamma, unsigned long long *counters,
                         hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// SSD fan-out lookup
+// ---------------------------------------------------------------------------
+struct FanoutArgs {
+    const int32_t *out_tokens;   // [B, gamma+1]
+    const int32_t *accept_len;   // [B]
+    const int32_t *cand;         // [B, gamma+1, f]
+    const int32_t *drafts;       // [B, (gamma+1) f, L] (may be null when out_next is)
+    int64_t B;
+    int32_t gamma, f, L;
+    int32_t *out_branch;         // [B]
+    int32_t *out_next;           // [B, L] or null
+    unsigned long long *counters;  // [2] or null: lookups, hits
+};
+hipError_t launch_fanout(const FanoutArgs &a, hipStream_t st);
+
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,
 // with K = counter_region(W) -- a function of W alone.  Every call returns
 // its counters to zero, and no call ever writes data below K, so calls of any

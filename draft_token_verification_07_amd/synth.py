@@ -31,6 +31,8 @@ Workloads (sizes are parameters; the defaults are the full sizes):
                  blog's 32-node, depth-5, top-k-8 tree).
   draft          B=64 rows, V=151936, bf16, shaped like sample_topp's rows; T=0.8,
                  top-p 0.9, top-k 50 (the draft-side sampler).
+  fanout         B=64, gamma=7, f=3 candidates per accepted length, L=8 drafts per
+                 branch (the SSD fan-out lookup).
 """
 from __future__ import annotations
 
@@ -151,6 +153,26 @@ def draft(seed: int, B: int = 64, V: int = 151936, spike_frac: float = 0.01, tem
                 temperature=temperature, top_p=top_p, top_k=top_k, d2t=None)
 
 
+def fanout(seed: int, B: int = 64, gamma: int = 7, f: int = 3, L: int = 8, V: int = 128256,
+           p_hit: float = 0.6) -> dict:
+    """SSD fan-out lookup input: verification outputs (accepted lengths and
+    emitted tokens), f candidate tokens per accepted length (the emitted one
+    among them with probability p_hit) and L pre-drafted tokens per branch
+    (the SSD guide's EAGLE run: k = 7, f = 3)."""
+    rng = np.random.default_rng(seed)
+    n = rng.integers(0, gamma + 1, B).astype(np.int32)
+    ot = np.full((B, gamma + 1), -1, np.int32)
+    emitted = rng.integers(0, V, B).astype(np.int32)
+    for b in range(B):
+        ot[b, :n[b]] = rng.integers(0, V, n[b])
+        ot[b, n[b]] = emitted[b]
+    cand = rng.integers(0, V, (B, gamma + 1, f)).astype(np.int32)
+    hit = rng.random(B) < p_hit
+    cand[np.flatnonzero(hit), n[hit], rng.integers(0, f, hit.sum())] = emitted[hit]
+    drafts = rng.integers(0, V, (B, (gamma + 1) * f, L)).astype(np.int32)
+    return dict(kind="fanout", out_tokens=ot, accept_len=n, cand=cand, drafts=drafts)
+
+
 def tree_topology(rng: np.random.Generator, N: int = 32, max_depth: int = 5, max_children: int = 8):
     """Random parent array: node 0 is the root; node k picks a parent uniformly
     among earlier nodes with depth < max_depth and fewer than max_children children."""
@@ -187,4 +209,5 @@ WORKLOADS = {
     "eagle_d2t": eagle_d2t,
     "tree": tree,
     "draft": draft,
+    "fanout": fanout,
 }

@@ -245,6 +245,35 @@ sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma,
                             hipStream_t stream);
 
 /*
+ * SSD fan-out lookup (SSD guide sec. 1: while the target verifies, the draft
+ * pre-speculates the possible verification outcomes and drafts every branch
+ * at once; a branch that matches the outcome makes the next round's drafting
+ * free.  sec. 7 runs it with a fan-out of 3).  After a verification call, the
+ * outcome of sequence b is (n, t) = (accept_len[b], out_tokens[b, n]).
+ *   out_tokens     [B, gamma+1] int32 and accept_len [B] int32: the outputs
+ *                  of spec_verify_sample / spec_verify_greedy.
+ *   cand           [B, gamma+1, f] int32: the f candidate tokens
+ *                  pre-speculated for each accepted length n (-1 = empty).
+ *   branch_drafts  [B, (gamma+1) * f, L] int32: the L tokens drafted ahead
+ *                  for branch n * f + j.  May be NULL when out_next is.
+ *   out_branch     [B] int32: n * f + j for the lowest slot j with
+ *                  cand[b, n, j] == t, -1 when none matches or n is outside
+ *                  [0, gamma] (a miss: the next round drafts anew).
+ *   out_next       [B, L] int32 or NULL: the matching branch's drafts, -1 on
+ *                  a miss.
+ *   counters       [2] uint64 or NULL (device, zeroed by the caller once):
+ *                  += lookups, += hits (64-bit atomic adds).
+ * Limits: f <= SV_MAX_FANOUT, L <= SV_MAX_BRANCH_DRAFTS.  No workspace.
+ * Errors: SV_ERR_INVALID_ARG (negative sizes, f < 1, null required
+ * pointers, counters not 8-byte aligned), SV_ERR_TOO_LARGE, SV_ERR_HIP.
+ */
+#define SV_MAX_FANOUT        64
+#define SV_MAX_BRANCH_DRAFTS 4096
+sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_len, const int32_t *cand,
+                             const int32_t *branch_drafts, int32_t B, int32_t gamma, int32_t f, int32_t L,
+                             int32_t *out_branch, int32_t *out_next, uint64_t *counters, hipStream_t stream);
+
+/*
  * Sampling verification without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs and results are those

@@ -54,6 +54,7 @@ def _load():
         lib.oracle_row_dist.argtypes = [P, i32, i32, f64, f64, i32, i32, P, P, P, P]
         lib.oracle_draft_sample.argtypes = [P, i32, P, P, i32, i32, f64, f64, i32, f64, P, P, P, P, P, P, P]
         lib.oracle_count.argtypes = [P, i32, i32, P]
+        lib.oracle_fanout_lookup.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P]
         lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, C.c_double, P, P]
         lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
         lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
@@ -178,6 +179,27 @@ def count(accept_len, gamma, counters=None):
     if rc != 0:
         raise ValueError("oracle_count: bad arguments")
     return c
+
+
+def fanout_lookup(out_tokens, accept_len, cand, drafts, counters=None):
+    """D10: SSD fan-out lookup.  out_tokens [B, g+1], accept_len [B], cand
+    [B, g+1, f], drafts [B, (g+1) f, L].  Returns (branch [B], next [B, L],
+    counters [2] = lookups, hits)."""
+    ot = np.ascontiguousarray(out_tokens, dtype=np.int32)
+    B, g1 = ot.shape
+    al = np.ascontiguousarray(accept_len, dtype=np.int32).reshape(B)
+    cd = np.ascontiguousarray(cand, dtype=np.int32)
+    f = cd.shape[2]
+    dr = np.ascontiguousarray(drafts, dtype=np.int32)
+    L = dr.shape[2]
+    br = np.empty(B, np.int32)
+    nx = np.empty((B, L), np.int32)
+    c = np.zeros(2, np.uint64) if counters is None else np.ascontiguousarray(counters, dtype=np.uint64).copy()
+    rc = _load().oracle_fanout_lookup(_ptr(ot), _ptr(al), _ptr(cd), _ptr(dr), B, g1 - 1, f, L, _ptr(br), _ptr(nx),
+                                      _ptr(c))
+    if rc != 0:
+        raise ValueError("oracle_fanout_lookup: bad arguments")
+    return br, nx, c
 
 
 def verify_greedy(logits, tokens):

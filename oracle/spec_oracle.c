@@ -579,6 +579,48 @@ int oracle_count(const int32_t *accept_len, int B, int gamma, uint64_t *counters
 }
 
 /* ------------------------------------------------------------------------- */
+/* D10: the SSD fan-out lookup.                                              */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [SSD guide] sec. 1: while the target verifies, the draft pre-speculates the
+ * possible verification outcomes and drafts every branch at once; a branch
+ * that matches the outcome makes the next round's drafting free.  sec. 7
+ * runs it with a fan-out of 3 (--f 3).  Here an outcome is the accepted length
+ * n and the token emitted after the accepted drafts, out_tokens[b, n]; for
+ * every n in [0, gamma] the table holds f candidate tokens cand[b, n, j], and
+ * branch n * f + j carries L pre-drafted tokens.
+ *   branch[b] = n * f + j for the lowest slot j with cand[b, n, j] equal to
+ *   the emitted token (and >= 0); -1 when none matches or n is outside
+ *   [0, gamma].  next[b, :] = that branch's drafts, -1 on a miss.
+ * counters [2] or NULL: += B lookups, += hits.
+ */
+int oracle_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_len, const int32_t *cand,
+                         const int32_t *drafts, int B, int gamma, int f, int L,
+                         int32_t *out_branch, int32_t *out_next, uint64_t *counters)
+{
+    if (B < 0 || gamma < 0 || f < 1 || L < 0) return ORC_EARG;
+    for (int b = 0; b < B; ++b) {
+        int32_t n = accept_len[b];
+        int32_t br = -1;
+        if (n >= 0 && n <= gamma) {
+            int32_t t = out_tokens[(size_t)b * (gamma + 1) + n];
+            for (int j = 0; j < f && br < 0; ++j) {
+                int32_t c = cand[((size_t)b * (gamma + 1) + n) * f + j];
+                if (c >= 0 && c == t) br = n * f + j;
+            }
+        }
+        out_branch[b] = br;
+        if (out_next)
+            for (int i = 0; i < L; ++i)
+                out_next[(size_t)b * L + i] =
+                    br >= 0 ? drafts[((size_t)b * (gamma + 1) * f + br) * L + i] : -1;
+        if (counters) { counters[0] += 1; counters[1] += br >= 0; }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* D7: greedy (temperature 0) verification.                                  */
 /* ------------------------------------------------------------------------- */
 

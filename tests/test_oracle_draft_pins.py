@@ -169,3 +169,62 @@ def test_counters_accumulate(oracle_mod):
         c = oracle_mod.count(a, 6, c)
         tot += [33, 33 * 6, a.sum(), a.sum() + 33, 0]
     assert c.tolist() == tot.tolist()
+
+
+# --------------------------------------------------------------------------
+# SSD fan-out lookup (SSD guide sec. 1 and sec. 7)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", GOLDEN["fanout_cases"], ids=lambda c: c["name"])
+def test_golden_fanout(oracle_mod, case):
+    g, f, L = case["gamma"], case["f"], case["L"]
+    B = len(case["accept_len"])
+    drafts = np.arange(B * (g + 1) * f * L, dtype=np.int32).reshape(B, (g + 1) * f, L) + 1000
+    br, nx, c = oracle_mod.fanout_lookup(np.array(case["out_tokens"], np.int32), np.array(case["accept_len"], np.int32),
+                                         np.array(case["cand"], np.int32), drafts)
+    e = case["expect"]
+    assert br[0] == e["branch"]
+    assert nx[0].tolist() == (drafts[0, e["branch"]].tolist() if e["branch"] >= 0 else [-1] * L)
+    assert c.tolist() == [1, int(e["branch"] >= 0)]
+
+
+def test_fanout_against_numpy(oracle_mod):
+    """Random tables: the branch is n*f + the first j (numpy argmax over the
+    match mask) whose candidate equals the emitted token."""
+    rng = np.random.default_rng(908)
+    B, g, f, L, V = 500, 5, 3, 4, 20
+    ot = rng.integers(0, V, (B, g + 1)).astype(np.int32)
+    n = rng.integers(-1, g + 2, B).astype(np.int32)
+    cand = rng.integers(-1, V, (B, g + 1, f)).astype(np.int32)
+    drafts = rng.integers(0, 1000, (B, (g + 1) * f, L)).astype(np.int32)
+    br, nx, c = oracle_mod.fanout_lookup(ot, n, cand, drafts)
+    hits = 0
+    for b in range(B):
+        if not 0 <= n[b] <= g:
+            assert br[b] == -1 and (nx[b] == -1).all()
+            continue
+        m = (cand[b, n[b]] == ot[b, n[b]]) & (cand[b, n[b]] >= 0)
+        if m.any():
+            j = int(np.argmax(m))
+            assert br[b] == n[b] * f + j
+            np.testing.assert_array_equal(nx[b], drafts[b, br[b]])
+            hits += 1
+        else:
+            assert br[b] == -1 and (nx[b] == -1).all()
+    assert c.tolist() == [B, hits] and 0 < hits < B
+
+
+def test_fanout_hits_when_branches_hold_the_argmax(oracle_mod):
+    """Greedy verification emits the target argmax at position n; a branch
+    table whose candidates at every n include that row's argmax always hits."""
+    w = synth.greedy(909, B=40, gamma=4, V=300)
+    out = oracle_mod.verify_greedy(w["target"], w["tokens"])
+    gm = np.argmax(synth.bf16_to_f32(w["target"]), axis=-1)            # [B, g+1]
+    rng = np.random.default_rng(910)
+    f = 3
+    cand = rng.integers(0, 300, (40, 5, f)).astype(np.int32)
+    slot = rng.integers(0, f, (40, 5))
+    cand[np.arange(40)[:, None], np.arange(5)[None], slot] = gm
+    br, _, c = oracle_mod.fanout_lookup(out["tokens"], out["accept_len"], cand, np.zeros((40, 5 * f, 1), np.int32))
+    assert (br >= 0).all() and c[1] == 40
+    assert ((br // f) == out["accept_len"]).all()
