@@ -55,6 +55,7 @@ def _load():
         lib.oracle_draft_sample.argtypes = [P, i32, P, P, i32, i32, f64, f64, i32, f64, P, P, P, P, P, P, P]
         lib.oracle_count.argtypes = [P, i32, i32, P]
         lib.oracle_fanout_lookup.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P]
+        lib.oracle_vocab_trim.argtypes = [P, C.c_int64, i32, f64, P, P, P, P]
         lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, C.c_double, P, P]
         lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
         lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
@@ -200,6 +201,21 @@ def fanout_lookup(out_tokens, accept_len, cand, drafts, counters=None):
     if rc != 0:
         raise ValueError("oracle_fanout_lookup: bad arguments")
     return br, nx, c
+
+
+def vocab_trim(tokens, Vt, P):
+    """D11: vocabulary trim.  Returns (d2t [Vd] ascending, t2d [Vt], info =
+    (kept mass, valid tokens, invalid tokens))."""
+    tk = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    d2t = np.empty(Vt, np.int32)
+    t2d = np.empty(Vt, np.int32)
+    vd = np.zeros(1, np.int32)
+    info = np.zeros(3, np.int64)
+    rc = _load().oracle_vocab_trim(_ptr(tk), tk.shape[0], int(Vt), float(np.float32(P)), _ptr(d2t), _ptr(t2d),
+                                   _ptr(vd), _ptr(info))
+    if rc != 0:
+        raise ValueError("oracle_vocab_trim: bad arguments")
+    return d2t[:vd[0]].copy(), t2d, info
 
 
 def verify_greedy(logits, tokens):

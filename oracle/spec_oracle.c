@@ -621,6 +621,75 @@ int oracle_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_len, c
 }
 
 /* ------------------------------------------------------------------------- */
+/* D11: the vocabulary-trim d2t builder.                                     */
+/* ------------------------------------------------------------------------- */
+
+typedef struct {
+    int64_t count;
+    int32_t id;
+} cid_t;
+
+/* Larger count first, then lower id: a total order. */
+static int cmp_count_desc(const void *a, const void *b)
+{
+    const cid_t *x = (const cid_t *)a, *y = (const cid_t *)b;
+    if (x->count > y->count) return -1;
+    if (x->count < y->count) return 1;
+    return (x->id < y->id) ? -1 : (x->id > y->id);
+}
+
+/*
+ * [Eagle blog] sec. 6: from the token frequencies of a corpus, keep the core
+ * vocabulary whose cumulative probability reaches P >= 0.95; the draft head
+ * then scores only those ids ([SSD guide] sec. 6 maps them back through d2t).
+ *   counts c[t] of the ids t in [0, Vt) in tokens[0..N) (others are invalid);
+ *   order the ids by count descending, lower id first on equal counts;
+ *   keep the smallest prefix whose count sum reaches P * Nv, Nv = the valid
+ *   tokens (P * Nv in float64); ids of count 0 are never kept, so P >= 1
+ *   keeps every observed id.
+ * out_d2t [Vt]: the kept ids in ascending order in its first *out_vd entries;
+ * out_t2d [Vt] or NULL: position of t in d2t, -1 when t is not kept;
+ * out_info [3] or NULL: kept count mass, valid tokens, invalid tokens.
+ */
+int oracle_vocab_trim(const int32_t *tokens, int64_t N, int Vt, double P, int32_t *out_d2t,
+                      int32_t *out_t2d, int32_t *out_vd, int64_t *out_info)
+{
+    if (N < 0 || Vt < 1 || !(P > 0.0)) return ORC_EARG;
+    cid_t *c = calloc((size_t)Vt, sizeof(cid_t));
+    if (!c) return ORC_EMEM;
+    int64_t valid = 0, invalid = 0;
+    for (int t = 0; t < Vt; ++t) c[t].id = t;
+    for (int64_t i = 0; i < N; ++i) {
+        int32_t t = tokens[i];
+        if (t < 0 || t >= Vt) { ++invalid; continue; }
+        c[t].count += 1;
+        ++valid;
+    }
+    qsort(c, (size_t)Vt, sizeof(cid_t), cmp_count_desc);
+    double T = P * (double)valid;
+    int k = 0;
+    int64_t cum = 0;
+    while (k < Vt && c[k].count > 0 && !((double)cum >= T)) {
+        cum += c[k].count;
+        ++k;
+    }
+    /* ascending ids of the first k positions */
+    unsigned char *keep = calloc((size_t)Vt, 1);
+    if (!keep) { free(c); return ORC_EMEM; }
+    for (int s = 0; s < k; ++s) keep[c[s].id] = 1;
+    int pos = 0;
+    for (int t = 0; t < Vt; ++t) {
+        if (out_t2d) out_t2d[t] = keep[t] ? pos : -1;
+        if (keep[t]) out_d2t[pos++] = t;
+    }
+    *out_vd = k;
+    if (out_info) { out_info[0] = cum; out_info[1] = valid; out_info[2] = invalid; }
+    free(keep);
+    free(c);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* D7: greedy (temperature 0) verification.                                  */
 /* ------------------------------------------------------------------------- */
 

@@ -228,3 +228,69 @@ def test_fanout_hits_when_branches_hold_the_argmax(oracle_mod):
     br, _, c = oracle_mod.fanout_lookup(out["tokens"], out["accept_len"], cand, np.zeros((40, 5 * f, 1), np.int32))
     assert (br >= 0).all() and c[1] == 40
     assert ((br // f) == out["accept_len"]).all()
+
+
+# --------------------------------------------------------------------------
+# Vocabulary-trim d2t builder (EAGLE blog sec. 6)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", GOLDEN["vocab_trim_cases"], ids=lambda c: c["name"])
+def test_golden_vocab_trim(oracle_mod, case):
+    d2t, t2d, info = oracle_mod.vocab_trim(np.array(case["tokens"], np.int32), case["Vt"], case["P"])
+    e = case["expect"]
+    assert d2t.tolist() == e["d2t"] and len(d2t) == e["vd"]
+    assert info.tolist() == [e["mass"], e["valid"], e["invalid"]]
+    assert [t2d[t] for t in e["d2t"]] == list(range(e["vd"]))
+    assert (np.delete(t2d, e["d2t"]) == -1).all()
+
+
+def test_vocab_trim_against_numpy(oracle_mod):
+    """Random skewed streams: numpy bincount, lexsort (count desc, id asc),
+    cumsum and searchsorted give the same kept set."""
+    rng = np.random.default_rng(911)
+    for trial in range(200):
+        Vt = int(rng.integers(1, 300))
+        N = int(rng.integers(0, 3000))
+        ranks = rng.permutation(Vt)
+        tok = ranks[np.minimum(rng.zipf(1.3, N) - 1, Vt - 1)].astype(np.int32)
+        tok[rng.random(N) < 0.01] = Vt + 3                               # a few invalid ids
+        P = float(rng.choice([0.1, 0.5, 0.9, 0.95, 0.999, 1.0]))
+        d2t, t2d, info = oracle_mod.vocab_trim(tok, Vt, P)
+        v = tok[(tok >= 0) & (tok < Vt)]
+        cnt = np.bincount(v, minlength=Vt)
+        order = np.lexsort((np.arange(Vt), -cnt))
+        cum = np.cumsum(cnt[order])
+        T = float(np.float32(P)) * len(v)
+        nz = int((cnt > 0).sum())
+        k = min(int(np.searchsorted(cum, T, side="left")) + 1, nz) if len(v) else 0
+        assert d2t.tolist() == sorted(order[:k].tolist())
+        assert info.tolist() == [int(cnt[order[:k]].sum()), len(v), N - len(v)]
+        assert (np.diff(d2t) > 0).all()
+
+
+def test_vocab_trim_limits(oracle_mod):
+    rng = np.random.default_rng(912)
+    tok = rng.integers(0, 50, 1000).astype(np.int32)
+    cnt = np.bincount(tok, minlength=50)
+    # P -> 0 keeps the single most frequent id (lowest id on ties); P = 1 keeps every observed id
+    d2t, _, _ = oracle_mod.vocab_trim(tok, 50, 1e-9)
+    assert d2t.tolist() == [int(np.argmax(cnt))]
+    d2t, _, _ = oracle_mod.vocab_trim(tok, 50, 1.0)
+    assert d2t.tolist() == np.flatnonzero(cnt).tolist()
+    d2t, _, _ = oracle_mod.vocab_trim(np.zeros(0, np.int32), 50, 0.95)
+    assert d2t.tolist() == []
+
+
+def test_vocab_trim_feeds_verification(oracle_mod):
+    """The built map is a valid d2t: verification with it sets no map status."""
+    rng = np.random.default_rng(913)
+    Vt = 500
+    tok = rng.permutation(Vt)[np.minimum(rng.zipf(1.2, 20000) - 1, Vt - 1)].astype(np.int32)
+    d2t, _, _ = oracle_mod.vocab_trim(tok, Vt, 0.95)
+    Vd = len(d2t)
+    assert 0 < Vd < Vt
+    zt = rng.standard_normal((2, 3, Vt)).astype(np.float32)
+    zd = rng.standard_normal((2, 2, Vd)).astype(np.float32)
+    out = oracle_mod.verify_sample(zt, zd, d2t[rng.integers(0, Vd, (2, 2))], synth.uniforms(rng, (2, 2)),
+                                   synth.uniforms(rng, (2,)), 1.0, 1.0, d2t=d2t)
+    assert (out["status"] & oracle_mod.ST_D2T == 0).all()
