@@ -23,7 +23,8 @@ the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
 launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
 the same workload (one thread and every host core).  The default run then
 times the other workloads the same way (the four other verification
-configurations, the draft-side sampler and the SSD fan-out lookup) and reports each under
+configurations, the draft-side sampler, the SSD fan-out lookup and the
+vocabulary trim) and reports each under
 config.workloads (step time, rows/s, GB/s and fraction of peak, counter
 traffic, the oracle's rows/s).
 """
@@ -53,6 +54,7 @@ WORKLOADS = {
     "tree": dict(desc="greedy tree verify, B=16 N=32 V=49152 bf16"),
     "draft": dict(desc="draft-side sampler, B=64 V=151936 bf16, T=0.8 top_p=0.9 top_k=50"),
     "fanout": dict(desc="SSD fan-out lookup, B=64 gamma=7 f=3 L=8"),
+    "trim": dict(desc="vocabulary-trim d2t builder, 2^24 Zipf(1.1) tokens over Vt=128256, P=0.95"),
 }
 
 
@@ -61,6 +63,9 @@ def compulsory_bytes(w) -> int:
     if w["kind"] == "draft":
         B = w["logits"].shape[0]
         return int(w["logits"].nbytes + w["u"].nbytes + 3 * B * 4)       # logits, uniforms; token, prob, status
+    if w["kind"] == "trim":
+        # the token stream read once; d2t, t2d, the kept count and the info written
+        return int(w["tokens"].nbytes + 2 * 4 * w["Vt"] + 4 + 24)
     if w["kind"] == "fanout":
         B, g1, f = w["cand"].shape
         L = w["drafts"].shape[2]
@@ -83,6 +88,8 @@ def compulsory_bytes(w) -> int:
 
 
 def rows_per_step(w) -> int:
+    if w["kind"] == "trim":
+        return int(w["tokens"].shape[0])
     if w["kind"] == "fanout":
         return int(w["cand"].shape[0])
     if w["kind"] == "draft":
@@ -111,6 +118,11 @@ def device_sets(w, nrot, dev):
             return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a.copy()).to(dev)
 
+    if w["kind"] == "trim":
+        base = dict(tokens=t(w["tokens"]))
+        sets = [base] + [dict(tokens=base["tokens"].clone()) for _ in range(nrot - 1)]
+        torch.cuda.synchronize()
+        return sets
     if w["kind"] == "fanout":
         base = {k: t(w[k]) for k in ("out_tokens", "accept_len", "cand", "drafts")}
         torch.cuda.synchronize()
@@ -138,7 +150,7 @@ def device_sets(w, nrot, dev):
 
 
 def _batch(w) -> int:
-    key = {"draft": "logits", "fanout": "cand"}.get(w["kind"], "target")
+    key = {"draft": "logits", "fanout": "cand", "trim": "tokens"}.get(w["kind"], "target")
     return int(w[key].shape[0])
 
 
@@ -164,6 +176,10 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float, threads: int):
     sl = slice(0, s)
 
     def one_pass():
+        if w["kind"] == "trim":
+            n = min(w["tokens"].shape[0], 1 << 20)
+            oracle.vocab_trim(w["tokens"][:n], w["Vt"], w["P"])
+            return n, 1
         if w["kind"] == "fanout":
             oracle.fanout_lookup(w["out_tokens"][sl], w["accept_len"][sl], w["cand"][sl], w["drafts"][sl])
             return s, 1
@@ -200,6 +216,12 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
     one = cpu_baseline(w, max(1, max_seqs // 8), work_seconds, 1)
     many = cpu_baseline(w, max_seqs, work_seconds, ncores) if w["kind"] == "sample" and ncores > 1 else one
     B = _batch(w)
+    if w["kind"] == "trim":
+        n = min(B, 1 << 20)
+        return dict(value=one["value"], unit="tokens/s", cores=1, kind="oracle", value_1thread=one["value"],
+                    cores_available=ncores, nproc=os.cpu_count(), cpu_model=cpu_model(),
+                    sample="1 thread: %d pass(es) over the first %d of %d tokens, %.2f s wall"
+                           % (one["passes"], n, B, one["wall_s"]))
     return dict(value=many["value"], unit="rows/s", cores=many["cores"], kind="oracle",
                 value_1thread=one["value"], cores_available=ncores, nproc=os.cpu_count(), cpu_model=cpu_model(),
                 sample="1 thread: %d pass(es) over the first %d of %d sequences, %.2f s wall; "
@@ -210,7 +232,8 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
 
 KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
-               tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel")
+               tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel",
+               trim="trim_hist_kernel+trim_select_kernel")
 
 
 def measure(name, args, dev, log):
@@ -227,7 +250,15 @@ def measure(name, args, dev, log):
     stream = torch.cuda.current_stream(dev)
 
     # preallocated outputs and one workspace (calls on one stream share it)
-    if w["kind"] == "fanout":
+    if w["kind"] == "trim":
+        Vt = w["Vt"]
+        need = sv.sv_workspace_bytes_vocab_trim(Vt)
+        outs = (torch.empty(Vt, dtype=torch.int32, device=dev), torch.empty(Vt, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+
+        def step(s):
+            sv.spec_vocab_trim(s["tokens"], Vt, w["P"], ws=ws, out=outs)
+    elif w["kind"] == "fanout":
         need = 256
         ctr = torch.zeros(2, dtype=torch.int64, device=dev)
 
@@ -315,7 +346,7 @@ def measure(name, args, dev, log):
     # launch-to-launch duration (for the multi-kernel paths, of the call).
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     res = dict(workload=name, desc=WORKLOADS[name]["desc"], kernel=KERNELS[name],
-               logits_dtype=("-" if w["kind"] == "fanout" else
+               logits_dtype=("-" if w["kind"] in ("fanout", "trim") else
                              str((w["logits"] if w["kind"] == "draft" else w["target"]).dtype).replace("uint16", "bf16")),
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
                ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
@@ -384,7 +415,7 @@ def main():
 
     head = args.workload
     names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp",
-                                                         "draft", "fanout") if n != head])
+                                                         "draft", "fanout", "trim") if n != head])
     results, inputs = {}, {}
     for name in names:
         inputs[name], results[name] = measure(name, args, dev, log)

@@ -87,6 +87,10 @@ def lib() -> C.CDLL:
                 L.spec_verify_count.argtypes = [P, i32, i32, P, P]
                 L.spec_fanout_lookup.restype = C.c_int
                 L.spec_fanout_lookup.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P]
+                L.sv_workspace_bytes_vocab_trim.restype = sz
+                L.sv_workspace_bytes_vocab_trim.argtypes = [i32]
+                L.spec_vocab_trim.restype = C.c_int
+                L.spec_vocab_trim.argtypes = [P, C.c_int64, i32, C.c_float, P, P, P, P, P, sz, P]
                 L.spec_verify_tree_greedy.restype = C.c_int
                 L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
                 _lib = L
@@ -315,6 +319,29 @@ def spec_fanout_lookup(out_tokens, accept_len, cand, branch_drafts=None, *, coun
                                Ln, _ptr(br), _ptr(nx), _ptr(counters), _stream(dev))
     _raise("spec_fanout_lookup", rc)
     return br, nx
+
+
+def sv_workspace_bytes_vocab_trim(Vt) -> int:
+    return int(lib().sv_workspace_bytes_vocab_trim(Vt))
+
+
+def spec_vocab_trim(tokens, Vt: int, P: float = 0.95, *, ws: torch.Tensor | None = None, out=None):
+    """Vocabulary-trim d2t builder.  Returns (d2t [Vt] int32 -- the first vd
+    entries valid --, t2d [Vt] int32, vd [1] int32, info [3] int64) device
+    tensors (no host synchronization)."""
+    L = lib()
+    dev = tokens.device
+    _check(tokens, "tokens", dev, torch.int32)
+    if out is None:
+        out = (torch.empty(Vt, dtype=torch.int32, device=dev), torch.empty(Vt, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev), torch.empty(3, dtype=torch.int64, device=dev))
+    need = sv_workspace_bytes_vocab_trim(Vt)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_vocab_trim(_ptr(tokens), tokens.numel(), int(Vt), float(P), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                           _ptr(out[3]), _ptr(ws), ws.numel(), _stream(dev))
+    _raise("spec_vocab_trim", rc)
+    return out
 
 
 def spec_verify_greedy(target_logits, draft_tokens, *, ws: torch.Tensor | None = None, out=None):

@@ -329,6 +329,35 @@ sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_le
     return launch_fanout(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+size_t sv_workspace_bytes_vocab_trim(int32_t Vt) {
+    if (Vt < 1 || Vt > SV_MAX_VOCAB) return 0;
+    return workspace_need(trim_counter_bytes(Vt), 256);
+}
+
+sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P, int32_t *out_d2t,
+                          int32_t *out_t2d, int32_t *out_vd, int64_t *out_info, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    if (N < 0 || Vt < 1 || !(P > 0.0f)) return SV_ERR_INVALID_ARG;
+    if (Vt > SV_MAX_VOCAB || N > (int64_t)INT32_MAX) return SV_ERR_TOO_LARGE;
+    if ((N > 0 && !tokens) || !out_d2t || !out_vd || !workspace) return SV_ERR_INVALID_ARG;
+    if (out_info && !aligned(out_info, sizeof(int64_t))) return SV_ERR_INVALID_ARG;
+    const size_t cb = trim_counter_bytes(Vt);
+    if (!workspace_fits(workspace_bytes, cb, 256)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    TrimArgs a;
+    a.tokens = tokens;
+    a.N = N;
+    a.Vt = Vt;
+    a.P = P;
+    a.out_d2t = out_d2t;
+    a.out_t2d = out_t2d;
+    a.out_vd = out_vd;
+    a.out_info = out_info;
+    char *base = static_cast<char *>(workspace);
+    a.counts = reinterpret_cast<uint32_t *>(base);
+    a.totals = reinterpret_cast<unsigned long long *>(base + align256(sizeof(uint32_t) * (size_t)Vt));
+    return launch_trim(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 sv_status spec_verify_sample_noalloc(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
                                      sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
                                      const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,

@@ -229,6 +229,24 @@ struct FanoutArgs {
 };
 hipError_t launch_fanout(const FanoutArgs &a, hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Vocabulary-trim d2t builder
+// ---------------------------------------------------------------------------
+struct TrimArgs {
+    const int32_t *tokens;        // [N]
+    int64_t N;
+    int32_t Vt;
+    float P;
+    int32_t *out_d2t;             // [Vt]: the kept ids ascending in the first *out_vd entries
+    int32_t *out_t2d;             // [Vt] or null
+    int32_t *out_vd;              // [1]
+    int64_t *out_info;            // [3] or null: kept mass, valid tokens, invalid tokens
+    uint32_t *counts;             // [Vt] (counter region; returned to zero)
+    unsigned long long *totals;   // [2] valid, invalid (counter region; returned to zero)
+};
+size_t trim_counter_bytes(int32_t Vt);
+hipError_t launch_trim(const TrimArgs &a, hipStream_t st);
+
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,
 // with K = counter_region(W) -- a function of W alone.  Every call returns
 // its counters to zero, and no call ever writes data below K, so calls of any

@@ -33,6 +33,8 @@ Workloads (sizes are parameters; the defaults are the full sizes):
                  top-p 0.9, top-k 50 (the draft-side sampler).
   fanout         B=64, gamma=7, f=3 candidates per accepted length, L=8 drafts per
                  branch (the SSD fan-out lookup).
+  trim           2^24 token ids over Vt=128256 from a bounded Zipf law (s = 1.1) at
+                 random ids, P = 0.95 (the vocabulary trim; no corpus is used).
 """
 from __future__ import annotations
 
@@ -173,6 +175,23 @@ def fanout(seed: int, B: int = 64, gamma: int = 7, f: int = 3, L: int = 8, V: in
     return dict(kind="fanout", out_tokens=ot, accept_len=n, cand=cand, drafts=drafts)
 
 
+def token_stream(seed: int, N: int = 1 << 24, Vt: int = 128256, s: float = 1.1, invalid_frac: float = 0.0) -> dict:
+    """A corpus stand-in for the vocabulary trim: N token ids drawn from a
+    bounded Zipf law (p(rank r) proportional to r^-s over Vt ranks) with the
+    ranks placed at random ids, optionally with a fraction of ids outside
+    [0, Vt)."""
+    rng = np.random.default_rng(seed)
+    w = np.arange(1, Vt + 1, dtype=np.float64) ** -s
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    ranks = np.minimum(np.searchsorted(cdf, rng.random(N)), Vt - 1)
+    ids = rng.permutation(Vt).astype(np.int32)[ranks]
+    if invalid_frac > 0:
+        bad = rng.random(N) < invalid_frac
+        ids[bad] = Vt + rng.integers(0, 100, bad.sum())
+    return dict(kind="trim", tokens=ids, Vt=Vt, P=0.95)
+
+
 def tree_topology(rng: np.random.Generator, N: int = 32, max_depth: int = 5, max_children: int = 8):
     """Random parent array: node 0 is the root; node k picks a parent uniformly
     among earlier nodes with depth < max_depth and fewer than max_children children."""
@@ -210,4 +229,5 @@ WORKLOADS = {
     "tree": tree,
     "draft": draft,
     "fanout": fanout,
+    "trim": token_stream,
 }

@@ -274,6 +274,32 @@ sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_le
                              int32_t *out_branch, int32_t *out_next, uint64_t *counters, hipStream_t stream);
 
 /*
+ * Vocabulary-trim d2t builder (the 2.16x EAGLE blog sec. 6: from corpus token
+ * frequencies keep the core vocabulary whose cumulative probability reaches
+ * P >= 0.95, so the draft head scores fewer ids; SSD guide sec. 6 maps them
+ * back through d2t).  Ids of tokens[0..N) in [0, Vt) are counted (others are
+ * invalid), ordered by count descending with lower ids first, and the
+ * smallest prefix whose count sum reaches P * (valid tokens) is kept (in
+ * float64 from the float32 P); ids of count 0 are never kept, so P >= 1 keeps
+ * every observed id.
+ *   tokens     [N] int32 (device).  N <= INT32_MAX.
+ *   out_d2t    [Vt] int32: the kept ids in ascending order in its first
+ *              *out_vd entries -- a map spec_verify_sample accepts.
+ *   out_t2d    [Vt] int32 or NULL: the position of id t in d2t, -1 if not kept.
+ *   out_vd     [1] int32: the number of kept ids (device memory).
+ *   out_info   [3] int64 or NULL: kept count mass, valid tokens, invalid tokens.
+ *   workspace  >= sv_workspace_bytes_vocab_trim(Vt) bytes, zeroed once when
+ *              allocated (its counts are returned to zero by every call).
+ * Errors: SV_ERR_INVALID_ARG (N < 0, Vt < 1, P <= 0 or NaN, null required
+ * pointers), SV_ERR_TOO_LARGE (Vt > SV_MAX_VOCAB or N > INT32_MAX),
+ * SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP.
+ */
+size_t sv_workspace_bytes_vocab_trim(int32_t Vt);
+sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P, int32_t *out_d2t,
+                          int32_t *out_t2d, int32_t *out_vd, int64_t *out_info, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sampling verification without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs and results are those

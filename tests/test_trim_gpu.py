@@ -1,0 +1,92 @@
+"""GPU parity of the vocabulary-trim d2t builder (spec_vocab_trim) against
+the oracle, through the C ABI: d2t, t2d, the kept count and the counts info
+are bit-exact (the 2.16x EAGLE blog sec. 6: keep the ids whose cumulative
+frequency reaches P >= 0.95).  Streams are seeded synthetic Zipf draws; no
+corpus is used."""
+import numpy as np
+import pytest
+
+from draft_token_verification_07_amd import synth
+from helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(oracle_mod):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _say(*a):
+    print("[trim]", *a, flush=True)
+
+
+def run_trim(tokens, Vt, P, ws=None):
+    import torch
+    import draft_token_verification_07_amd as sv
+    d2t, t2d, vd, info = sv.spec_vocab_trim(to_dev(np.ascontiguousarray(tokens, np.int32)), Vt, P, ws=ws)
+    torch.cuda.synchronize()
+    n = int(vd.item())
+    return d2t.cpu().numpy()[:n], t2d.cpu().numpy(), info.cpu().numpy()
+
+
+def _check(oracle_mod, tokens, Vt, P, ws=None):
+    g = run_trim(tokens, Vt, P, ws)
+    o = oracle_mod.vocab_trim(tokens, Vt, P)
+    np.testing.assert_array_equal(g[0], o[0])
+    np.testing.assert_array_equal(g[1], o[1])
+    np.testing.assert_array_equal(g[2], o[2])
+    return o
+
+
+@pytest.mark.parametrize("N,Vt,s,P", [(0, 8, 1.1, 0.95), (20, 8, 1.0, 0.95), (100000, 1000, 1.2, 0.9),
+                                      (1 << 20, 128256, 1.1, 0.95), (3000001, 151936, 0.9, 0.8),
+                                      (500000, 4099, 1.5, 0.999), (200000, 50000, 1.1, 1.0)])
+def test_trim_parity(oracle_mod, N, Vt, s, P):
+    w = synth.token_stream(9400 + N % 1000, N=N, Vt=Vt, s=s, invalid_frac=0.001 if N > 100 else 0.0)
+    o = _check(oracle_mod, w["tokens"], Vt, P)
+    _say("N=%d Vt=%d s=%g P=%g: kept %d ids, mass %d of %d" % (N, Vt, s, P, len(o[0]), o[2][0], o[2][1]))
+
+
+def test_trim_ties_and_limits(oracle_mod):
+    rng = np.random.default_rng(9401)
+    tok = rng.permutation(np.repeat(np.arange(300, dtype=np.int32), 7))      # every id exactly 7 times
+    for P in (0.5, 0.1, 1e-6, 1.0, 0.95):
+        _check(oracle_mod, tok, 1000, P)
+    _check(oracle_mod, np.array([5, 5, 7, -1, 99999], np.int32), 10, 0.5)
+
+
+def test_trim_workspace_reuse(oracle_mod):
+    """One workspace, several calls of different sizes: the counts are back
+    at zero after every call."""
+    import torch
+    import draft_token_verification_07_amd as sv
+    ws = torch.zeros(sv.sv_workspace_bytes_vocab_trim(151936), dtype=torch.uint8, device="cuda")
+    for seed, N, Vt in ((9402, 400000, 151936), (9403, 1000, 77), (9404, 2000000, 128256), (9405, 10, 151936)):
+        w = synth.token_stream(seed, N=N, Vt=Vt)
+        _check(oracle_mod, w["tokens"], Vt, 0.95, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.sum().item()) == 0
+
+
+def test_trim_map_feeds_verification(oracle_mod):
+    """A map built on the GPU drives sampling verification: no map status,
+    and parity with the oracle as for any d2t workload."""
+    from helpers import compare_sample, run_sample
+    w = synth.token_stream(9406, N=1 << 20, Vt=32000, s=1.1)
+    d2t, _, _ = run_trim(w["tokens"], 32000, 0.95)
+    Vd = len(d2t)
+    assert 100 < Vd < 32000 and (np.diff(d2t) > 0).all()
+    rng = np.random.default_rng(9407)
+    B, g = 8, 4
+    zd = (rng.standard_normal((B, g, Vd)) * 2).astype(np.float32)
+    zt = (rng.standard_normal((B, g + 1, 32000)) - 4).astype(np.float32)
+    zt[:, :g, d2t] = zd + rng.standard_normal((B, g, Vd)).astype(np.float32)
+    ws = dict(kind="sample", target=synth.bf16_bits(zt), draft=zd, tokens=d2t[rng.integers(0, Vd, (B, g))],
+              u_accept=synth.uniforms(rng, (B, g)), u_sample=synth.uniforms(rng, (B,)), d2t=d2t.astype(np.int32),
+              temperature=1.0, top_p=1.0)
+    out = run_sample(ws)
+    assert not (out["status"] & 2).any()
+    compare_sample(ws, out, oracle_mod)
