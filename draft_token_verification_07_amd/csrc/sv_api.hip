@@ -331,7 +331,7 @@ sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_le
 
 size_t sv_workspace_bytes_vocab_trim(int32_t Vt) {
     if (Vt < 1 || Vt > SV_MAX_VOCAB) return 0;
-    return workspace_need(trim_counter_bytes(Vt), 256);
+    return workspace_need(trim_counter_bytes(Vt), trim_data_bytes(Vt));
 }
 
 sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P, int32_t *out_d2t,
@@ -342,7 +342,7 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
     if ((N > 0 && !tokens) || !out_d2t || !out_vd || !workspace) return SV_ERR_INVALID_ARG;
     if (out_info && !aligned(out_info, sizeof(int64_t))) return SV_ERR_INVALID_ARG;
     const size_t cb = trim_counter_bytes(Vt);
-    if (!workspace_fits(workspace_bytes, cb, 256)) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace_fits(workspace_bytes, cb, trim_data_bytes(Vt))) return SV_ERR_WORKSPACE_TOO_SMALL;
     TrimArgs a;
     a.tokens = tokens;
     a.N = N;
@@ -353,8 +353,11 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
     a.out_vd = out_vd;
     a.out_info = out_info;
     char *base = static_cast<char *>(workspace);
-    a.counts = reinterpret_cast<uint32_t *>(base);
-    a.totals = reinterpret_cast<unsigned long long *>(base + align256(sizeof(uint32_t) * (size_t)Vt));
+    char *data = base + counter_region(workspace_bytes);
+    a.S = trim_slices(Vt);
+    a.totals = reinterpret_cast<unsigned long long *>(base);
+    a.part = reinterpret_cast<uint32_t *>(data);
+    a.counts = reinterpret_cast<uint32_t *>(data + align256(sizeof(uint32_t) * (size_t)a.S * Vt));
     return launch_trim(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -172,11 +172,14 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
     const u32x4 *body = reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(row) +
                                                         (size_t)sp.head * E::kBytes);
     // U vectors per lane per round, all loaded before any is used; loads past
-    // the chunk repeat its last vector and are masked afterwards
-    for (int32_t v = lo + threadIdx.x; v < hi; v += U * NT) {
+    // the chunk repeat its last vector and are masked afterwards.  The first
+    // round is taken by every thread and followed by a workgroup maximum, so
+    // that the band starts near the chunk maximum rather than at each lane's
+    // first values (which would fill the band with early vectors).
+    auto round = [&](int32_t v, bool first) {
         u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[min(v + u * NT, hi - 1)]);
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(&body[max(lo, min(v + u * NT, hi - 1))]);
         float x[U][E::kPerVec], vm[U];
         float tm = -INFINITY;
 #pragma unroll
@@ -190,6 +193,11 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
                 vm[u] = fmaxf(vm[u], x[u][k]);
             }
             tm = fmaxf(tm, vm[u]);
+        }
+        if (first) {
+            const float wm = wave_max(tm);
+            if (lane == 0 && wm > -INFINITY) atomicMax(&s_maxkey, zkey(wm));
+            __syncthreads();
         }
         if (tm > m_l) {
             s_l = (m_l == -INFINITY) ? 0.0f : s_l * exp2_hw((m_l - tm) * c);
@@ -217,6 +225,10 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
                     s_cvid[pos] = v + u * NT;
                 }
             }
+    };
+    if (hi > lo) {
+        round(lo + (int32_t)threadIdx.x, true);
+        for (int32_t v = lo + (int32_t)threadIdx.x + U * NT; v < hi; v += U * NT) round(v, false);
     }
     MaxSum ms;
     ms.m = m_l;

@@ -241,10 +241,18 @@ struct TrimArgs {
     int32_t *out_t2d;             // [Vt] or null
     int32_t *out_vd;              // [1]
     int64_t *out_info;            // [3] or null: kept mass, valid tokens, invalid tokens
-    uint32_t *counts;             // [Vt] (counter region; returned to zero)
+    int32_t S;                    // stream slices
+    uint32_t *part;               // [S, Vt] partial histograms
+    uint32_t *counts;             // [Vt]
     unsigned long long *totals;   // [2] valid, invalid (counter region; returned to zero)
 };
+constexpr int kTrimBins = 16384;        // ids per partial-histogram workgroup (64 KiB of LDS)
+constexpr int kTrimTargetWgs = 256;     // ranges x slices
+constexpr int kTrimMaxSlices = 64;
+int32_t trim_ranges(int32_t Vt);
+int32_t trim_slices(int32_t Vt);
 size_t trim_counter_bytes(int32_t Vt);
+size_t trim_data_bytes(int32_t Vt);
 hipError_t launch_trim(const TrimArgs &a, hipStream_t st);
 
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,

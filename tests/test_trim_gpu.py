@@ -59,16 +59,18 @@ def test_trim_ties_and_limits(oracle_mod):
 
 
 def test_trim_workspace_reuse(oracle_mod):
-    """One workspace, several calls of different sizes: the counts are back
-    at zero after every call."""
+    """One workspace, several calls of different sizes: the totals in the
+    counter region are back at zero after every call."""
     import torch
     import draft_token_verification_07_amd as sv
-    ws = torch.zeros(sv.sv_workspace_bytes_vocab_trim(151936), dtype=torch.uint8, device="cuda")
+    need = sv.sv_workspace_bytes_vocab_trim(151936)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for seed, N, Vt in ((9402, 400000, 151936), (9403, 1000, 77), (9404, 2000000, 128256), (9405, 10, 151936)):
         w = synth.token_stream(seed, N=N, Vt=Vt)
         _check(oracle_mod, w["tokens"], Vt, 0.95, ws=ws)
     torch.cuda.synchronize()
-    assert int(ws.sum().item()) == 0
+    K = (need // 8) & ~255                          # the counter region of this workspace size
+    assert int(ws[:K].sum().item()) == 0
 
 
 def test_trim_map_feeds_verification(oracle_mod):
