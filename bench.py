@@ -23,8 +23,9 @@ the dominant kernel's roofline (algorithmic HBM bytes per launch / its mean
 launch time, against 8 TB/s), and the CPU oracle timed on a bounded sample of
 the same workload (one thread and every host core).  The default run then
 times the other workloads the same way (the four other verification
-configurations, the draft-side sampler, the SSD fan-out lookup and the
-vocabulary trim) and reports each under
+configurations, the draft-side sampler, the SSD fan-out lookup, the
+vocabulary trim and the fused lm_head -> greedy verification, the latter
+against the bf16 MFMA peak) and reports each under
 config.workloads (step time, rows/s, GB/s and fraction of peak, counter
 traffic, the oracle's rows/s).
 """
@@ -55,7 +56,9 @@ WORKLOADS = {
     "draft": dict(desc="draft-side sampler, B=64 V=151936 bf16, T=0.8 top_p=0.9 top_k=50"),
     "fanout": dict(desc="SSD fan-out lookup, B=64 gamma=7 f=3 L=8"),
     "trim": dict(desc="vocabulary-trim d2t builder, 2^24 Zipf(1.1) tokens over Vt=128256, P=0.95"),
+    "lmhead": dict(desc="fused lm_head -> greedy verify, hidden [128, 7, 4096] x W [128256, 4096] bf16"),
 }
+PEAK_BF16_TFLOPS = 2500.0
 
 
 def compulsory_bytes(w) -> int:
@@ -63,6 +66,10 @@ def compulsory_bytes(w) -> int:
     if w["kind"] == "draft":
         B = w["logits"].shape[0]
         return int(w["logits"].nbytes + w["u"].nbytes + 3 * B * 4)       # logits, uniforms; token, prob, status
+    if w["kind"] == "lmhead":
+        # hidden and W read once, draft tokens read; tokens, lengths, argmax, max logit, status written
+        B, R, d = w["hidden"].shape
+        return int(w["hidden"].nbytes + w["W"].nbytes + w["tokens"].nbytes + B * R * 4 + B * 4 + 2 * B * R * 4 + B * 4)
     if w["kind"] == "trim":
         # the token stream read once; d2t, t2d, the kept count and the info written
         return int(w["tokens"].nbytes + 2 * 4 * w["Vt"] + 4 + 24)
@@ -88,6 +95,8 @@ def compulsory_bytes(w) -> int:
 
 
 def rows_per_step(w) -> int:
+    if w["kind"] == "lmhead":
+        return int(w["hidden"].shape[0] * w["hidden"].shape[1])
     if w["kind"] == "trim":
         return int(w["tokens"].shape[0])
     if w["kind"] == "fanout":
@@ -118,6 +127,11 @@ def device_sets(w, nrot, dev):
             return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a.copy()).to(dev)
 
+    if w["kind"] == "lmhead":
+        # the weights (GBs) exceed the Infinity Cache: every step reads them from HBM
+        base = dict(hidden=t(w["hidden"]), W=t(w["W"]), tokens=t(w["tokens"]))
+        torch.cuda.synchronize()
+        return [base]
     if w["kind"] == "trim":
         base = dict(tokens=t(w["tokens"]))
         sets = [base] + [dict(tokens=base["tokens"].clone()) for _ in range(nrot - 1)]
@@ -150,7 +164,7 @@ def device_sets(w, nrot, dev):
 
 
 def _batch(w) -> int:
-    key = {"draft": "logits", "fanout": "cand", "trim": "tokens"}.get(w["kind"], "target")
+    key = {"draft": "logits", "fanout": "cand", "trim": "tokens", "lmhead": "hidden"}.get(w["kind"], "target")
     return int(w[key].shape[0])
 
 
@@ -176,6 +190,11 @@ def cpu_baseline(w, max_seqs: int, work_seconds: float, threads: int):
     sl = slice(0, s)
 
     def one_pass():
+        if w["kind"] == "lmhead":
+            R = w["hidden"].shape[1]
+            z, _ = oracle.lmhead_logits(w["hidden"][0], w["W"])
+            oracle.greedy_from_argmax(np.argmax(z, axis=1)[None], w["tokens"][:1], w["W"].shape[0])
+            return R, 1
         if w["kind"] == "trim":
             n = min(w["tokens"].shape[0], 1 << 20)
             oracle.vocab_trim(w["tokens"][:n], w["Vt"], w["P"])
@@ -233,7 +252,8 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
 KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
                tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel",
-               trim="trim_hist_kernel+trim_select_kernel")
+               trim="trim_part_kernel+trim_reduce_kernel+trim_select_kernel",
+               lmhead="lmhead_kernel+lmhead_reduce_kernel+seq_kernel")
 
 
 def measure(name, args, dev, log):
@@ -246,12 +266,21 @@ def measure(name, args, dev, log):
     w = make_inputs(name, args.seed)
     nbytes = compulsory_bytes(w)
     # rotated copies keep the bulk inputs cold; the fan-out tables are a few KB
-    nrot = 1 if w["kind"] == "fanout" else max(1, int(math.ceil(args.cold_bytes / nbytes)))
+    nrot = 1 if w["kind"] in ("fanout", "lmhead") else max(1, int(math.ceil(args.cold_bytes / nbytes)))
     sets = device_sets(w, nrot, dev)
     stream = torch.cuda.current_stream(dev)
 
     # preallocated outputs and one workspace (calls on one stream share it)
-    if w["kind"] == "trim":
+    if w["kind"] == "lmhead":
+        B, R, d = w["hidden"].shape
+        need = sv.sv_workspace_bytes_lmhead(B * R, w["W"].shape[0])
+        outs = (torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+                torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty((B, R), dtype=torch.float32, device=dev),
+                torch.empty(B, dtype=torch.int32, device=dev))
+
+        def step(s):
+            sv.spec_lmhead_verify_greedy(s["hidden"], s["W"], s["tokens"], ws=ws, out=outs)
+    elif w["kind"] == "trim":
         Vt = w["Vt"]
         need = sv.sv_workspace_bytes_vocab_trim(Vt)
         outs = (torch.empty(Vt, dtype=torch.int32, device=dev), torch.empty(Vt, dtype=torch.int32, device=dev),
@@ -347,7 +376,7 @@ def measure(name, args, dev, log):
     # launch-to-launch duration (for the multi-kernel paths, of the call).
     achieved = nbytes / (ms_per_step / 1e3) / 1e9
     res = dict(workload=name, desc=WORKLOADS[name]["desc"], kernel=KERNELS[name],
-               logits_dtype=("-" if w["kind"] in ("fanout", "trim") else
+               logits_dtype=("-" if w["kind"] in ("fanout", "trim", "lmhead") else
                              str((w["logits"] if w["kind"] == "draft" else w["target"]).dtype).replace("uint16", "bf16")),
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
                ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
@@ -357,7 +386,16 @@ def measure(name, args, dev, log):
                launch_ms_mean=float(np.mean(per_launch_ms)), launch_ms_median=float(np.median(per_launch_ms)),
                launch_ms_p10=float(np.percentile(per_launch_ms, 10)),
                launch_ms_p90=float(np.percentile(per_launch_ms, 90)))
-    log("[bench] %s: %.2f us/step, %.0f GB/s (%.3f of peak)" % (name, ms_per_step * 1e3, achieved, achieved / PEAK_GBS))
+    if w["kind"] == "lmhead":
+        B, R, d = w["hidden"].shape
+        flops = 2.0 * B * R * w["W"].shape[0] * d
+        tf = flops / (ms_per_step / 1e3) / 1e12
+        res.update(bound="mfma", flops_per_step=flops, achieved_TFLOPs=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        log("[bench] %s: %.2f us/step, %.0f TFLOP/s (%.3f of the bf16 MFMA peak), %.0f GB/s"
+            % (name, ms_per_step * 1e3, tf, tf / PEAK_BF16_TFLOPS, achieved))
+    else:
+        log("[bench] %s: %.2f us/step, %.0f GB/s (%.3f of peak)" % (name, ms_per_step * 1e3, achieved,
+                                                                   achieved / PEAK_GBS))
     return w, res
 
 
@@ -416,7 +454,7 @@ def main():
 
     head = args.workload
     names = [head] + ([] if args.only else [n for n in ("greedy", "eagle_d2t", "tree", "sample_plain", "sample_topp",
-                                                         "draft", "fanout", "trim") if n != head])
+                                                         "draft", "fanout", "trim", "lmhead") if n != head])
     results, inputs = {}, {}
     for name in names:
         inputs[name], results[name] = measure(name, args, dev, log)

@@ -91,6 +91,12 @@ def lib() -> C.CDLL:
                 L.sv_workspace_bytes_vocab_trim.argtypes = [i32]
                 L.spec_vocab_trim.restype = C.c_int
                 L.spec_vocab_trim.argtypes = [P, C.c_int64, i32, C.c_float, P, P, P, P, P, sz, P]
+                L.sv_workspace_bytes_lmhead.restype = sz
+                L.sv_workspace_bytes_lmhead.argtypes = [i32, i32]
+                L.spec_lmhead_verify_greedy.restype = C.c_int
+                L.spec_lmhead_verify_greedy.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, sz, P]
+                L.spec_lmhead_verify_tree.restype = C.c_int
+                L.spec_lmhead_verify_tree.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
                 L.spec_verify_tree_greedy.restype = C.c_int
                 L.spec_verify_tree_greedy.argtypes = [P, C.c_int, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
                 _lib = L
@@ -341,6 +347,69 @@ def spec_vocab_trim(tokens, Vt: int, P: float = 0.95, *, ws: torch.Tensor | None
     rc = L.spec_vocab_trim(_ptr(tokens), tokens.numel(), int(Vt), float(P), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
                            _ptr(out[3]), _ptr(ws), ws.numel(), _stream(dev))
     _raise("spec_vocab_trim", rc)
+    return out
+
+
+def sv_workspace_bytes_lmhead(M, V) -> int:
+    return int(lib().sv_workspace_bytes_lmhead(M, V))
+
+
+def _lmhead_common(hidden, W, what):
+    dev = hidden.device
+    _check(hidden, "hidden", dev, torch.bfloat16)
+    _check(W, "W", dev, torch.bfloat16)
+    if hidden.dim() != 3 or W.dim() != 2 or hidden.shape[2] != W.shape[1]:
+        raise ValueError("%s: hidden must be [B, R, d] and W [V, d]" % what)
+    return dev, hidden.shape[0], hidden.shape[1], hidden.shape[2], W.shape[0]
+
+
+def spec_lmhead_verify_greedy(hidden, W, draft_tokens, *, want_rows: bool = True,
+                              ws: torch.Tensor | None = None, out=None):
+    """Fused lm_head -> greedy chain verification.  hidden [B, g+1, d] bf16,
+    W [V, d] bf16.  Returns (tokens [B, g+1], accept_len [B], argmax [B, g+1]
+    | None, maxlogit [B, g+1] | None, status [B])."""
+    L = lib()
+    dev, B, R, d, V = _lmhead_common(hidden, W, "spec_lmhead_verify_greedy")
+    g = R - 1
+    if g > 0:
+        _check(draft_tokens, "draft_tokens", dev, torch.int32, (B, g))
+    if out is None:
+        out = (torch.empty((B, R), dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty((B, R), dtype=torch.int32, device=dev) if want_rows else None,
+               torch.empty((B, R), dtype=torch.float32, device=dev) if want_rows else None,
+               torch.empty(B, dtype=torch.int32, device=dev))
+    need = sv_workspace_bytes_lmhead(B * R, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_lmhead_verify_greedy(_ptr(hidden), _ptr(W), _ptr(draft_tokens if g > 0 else None), B, g, d, V,
+                                     _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(out[3]), _ptr(out[4]), _ptr(ws),
+                                     ws.numel(), _stream(dev))
+    _raise("spec_lmhead_verify_greedy", rc)
+    return out
+
+
+def spec_lmhead_verify_tree(hidden, W, node_tokens, parents, *, want_rows: bool = True,
+                            ws: torch.Tensor | None = None, out=None):
+    """Fused lm_head -> greedy tree verification.  hidden [B, N, d] bf16.
+    Returns (path [B, N], tokens [B, N], accept_len [B], argmax [B, N] | None,
+    maxlogit [B, N] | None, status [B])."""
+    L = lib()
+    dev, B, N, d, V = _lmhead_common(hidden, W, "spec_lmhead_verify_tree")
+    _check(node_tokens, "node_tokens", dev, torch.int32, (B, N))
+    _check(parents, "parents", dev, torch.int32, (B, N))
+    if out is None:
+        out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int32, device=dev) if want_rows else None,
+               torch.empty((B, N), dtype=torch.float32, device=dev) if want_rows else None,
+               torch.empty(B, dtype=torch.int32, device=dev))
+    need = sv_workspace_bytes_lmhead(B * N, V)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = L.spec_lmhead_verify_tree(_ptr(hidden), _ptr(W), _ptr(node_tokens), _ptr(parents), B, N, d, V, _ptr(out[0]),
+                                   _ptr(out[1]), _ptr(out[2]), _ptr(out[3]), _ptr(out[4]), _ptr(out[5]), _ptr(ws),
+                                   ws.numel(), _stream(dev))
+    _raise("spec_lmhead_verify_tree", rc)
     return out
 
 

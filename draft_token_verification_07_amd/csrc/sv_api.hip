@@ -361,6 +361,97 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
     return launch_trim(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+size_t sv_workspace_bytes_lmhead(int32_t M, int32_t V) {
+    if (M < 0 || V < 1 || V > SV_MAX_VOCAB) return 0;
+    const size_t nt = ((size_t)V + kLmTile - 1) / kLmTile;
+    return workspace_need(256, align256(sizeof(uint64_t) * (size_t)M * nt) + align256(sizeof(ArgMax) * (size_t)M));
+}
+
+namespace {
+sv_status run_lmhead(const void *hidden, const void *W, const int32_t *tokens, const int32_t *parents, int32_t B,
+                     int32_t R, int32_t d, int32_t V, bool tree, int32_t *out_path, int32_t *out_tokens,
+                     int32_t *out_len, int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *ws,
+                     size_t ws_bytes, hipStream_t st) {
+    const int64_t M = (int64_t)B * R;
+    if (M > INT32_MAX) return SV_ERR_TOO_LARGE;
+    const size_t need = sv_workspace_bytes_lmhead((int32_t)M, V);
+    const size_t nt = ((size_t)V + kLmTile - 1) / kLmTile;
+    const size_t part_bytes = align256(sizeof(uint64_t) * (size_t)M * nt);
+    if (!workspace_fits(ws_bytes, 256, part_bytes + align256(sizeof(ArgMax) * (size_t)M))) return SV_ERR_WORKSPACE_TOO_SMALL;
+    (void)need;
+    LmheadArgs L;
+    L.hidden = static_cast<const uint16_t *>(hidden);
+    L.W = static_cast<const uint16_t *>(W);
+    L.M = (int32_t)M;
+    L.d = d;
+    L.V = V;
+    L.mtiles = (int32_t)((M + kLmTile - 1) / kLmTile);
+    L.ntiles = (int32_t)nt;
+    L.ntiles8 = (int32_t)((nt + 7) / 8 * 8);
+    if (!grid_fits((int64_t)L.mtiles * L.ntiles8)) return SV_ERR_TOO_LARGE;
+    char *data = static_cast<char *>(ws) + counter_region(ws_bytes);
+    L.part = reinterpret_cast<uint64_t *>(data);
+    L.rowres = reinterpret_cast<ArgMax *>(data + part_bytes);
+    L.out_argmax = out_argmax;
+    L.out_maxlogit = out_maxlogit;
+    if (launch_lmhead(L, st) != hipSuccess) return SV_ERR_HIP;
+    GreedyArgs a;
+    a.logits = nullptr;
+    a.tokens = tokens;
+    a.parents = parents;
+    a.B = B;
+    a.rows_per_seq = R;
+    a.V = V;
+    a.chunks = 1;
+    a.tree = tree ? 1 : 0;
+    a.split_chunks = 0;
+    a.out_tokens = out_tokens;
+    a.out_len = out_len;
+    a.out_status = out_status;
+    a.out_path = out_path;
+    a.part = nullptr;
+    a.rowres = L.rowres;
+    a.counters = nullptr;
+    return launch_seq(a, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status lmhead_check(const void *hidden, const void *W, int32_t B, int32_t R, int32_t d, int32_t V) {
+    if (B < 0 || R < 1 || d < 8 || V < 1) return SV_ERR_INVALID_ARG;
+    if (d % 8 != 0) return SV_ERR_INVALID_ARG;
+    if (V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
+    if (B == 0) return SV_OK;
+    if (!hidden || !W || !aligned(hidden, 16) || !aligned(W, 16)) return SV_ERR_INVALID_ARG;
+    return SV_OK;
+}
+}  // namespace
+
+sv_status spec_lmhead_verify_greedy(const void *hidden, const void *W, const int32_t *draft_tokens, int32_t B,
+                                    int32_t gamma, int32_t d, int32_t V, int32_t *out_tokens, int32_t *out_accept_len,
+                                    int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (gamma < 0) return SV_ERR_INVALID_ARG;
+    if (gamma > SV_MAX_GAMMA) return SV_ERR_TOO_LARGE;
+    const sv_status c = lmhead_check(hidden, W, B, gamma + 1, d, V);
+    if (c != SV_OK || B == 0) return c;
+    if (!out_tokens || !out_accept_len || !workspace || (gamma > 0 && !draft_tokens)) return SV_ERR_INVALID_ARG;
+    return run_lmhead(hidden, W, draft_tokens, nullptr, B, gamma + 1, d, V, false, nullptr, out_tokens,
+                      out_accept_len, out_argmax, out_maxlogit, out_status, workspace, workspace_bytes, stream);
+}
+
+sv_status spec_lmhead_verify_tree(const void *hidden, const void *W, const int32_t *node_tokens,
+                                  const int32_t *parents, int32_t B, int32_t N, int32_t d, int32_t V,
+                                  int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
+                                  int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (N > SV_MAX_TREE_NODES) return SV_ERR_TOO_LARGE;
+    const sv_status c = lmhead_check(hidden, W, B, N, d, V);
+    if (c != SV_OK || B == 0) return c;
+    if (!node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len || !workspace)
+        return SV_ERR_INVALID_ARG;
+    return run_lmhead(hidden, W, node_tokens, parents, B, N, d, V, true, out_path_nodes, out_tokens, out_accept_len,
+                      out_argmax, out_maxlogit, out_status, workspace, workspace_bytes, stream);
+}
+
 sv_status spec_verify_sample_noalloc(const void *target_logits, sv_dtype target_dtype, const void *draft_logits,
                                      sv_dtype draft_dtype, const int32_t *draft_tokens, const int32_t *d2t,
                                      const float *u_accept, const float *u_sample, int32_t B, int32_t gamma,

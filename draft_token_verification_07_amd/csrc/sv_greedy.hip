@@ -293,6 +293,15 @@ int32_t greedy_chunks(int32_t V, int64_t rows) {
     return (int32_t)C;
 }
 
+// The sequence step alone, on row results already in a.rowres (one per row,
+// published): the chain or the tree walk, one workgroup per sequence.
+hipError_t launch_seq(const GreedyArgs &a, hipStream_t st) {
+    const size_t R = (size_t)a.rows_per_seq;
+    const size_t lds = 2 * R * sizeof(int32_t) + (a.tree ? R * (sizeof(int32_t) + sizeof(int16_t) + sizeof(uint8_t)) : 0);
+    hipLaunchKernelGGL((seq_kernel<kGreedyThreads>), dim3(a.B), dim3(kGreedyThreads), lds, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t st) {
     const int64_t grid = (int64_t)a.B * a.rows_per_seq * a.chunks;
     if (dtype == SV_BF16) return launch_greedy_dt<SV_BF16>(a, (int)grid, st);

@@ -110,6 +110,23 @@ struct GreedyArgs {
 int32_t greedy_chunks(int32_t V, int64_t rows);
 bool greedy_split(int32_t R, int32_t C);
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t st);
+hipError_t launch_seq(const GreedyArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Fused lm_head -> greedy verification
+// ---------------------------------------------------------------------------
+struct LmheadArgs {
+    const uint16_t *hidden;     // [M, d] bfloat16 bits, M = B * R
+    const uint16_t *W;          // [V, d] bfloat16 bits
+    int32_t M, d, V;
+    int32_t mtiles, ntiles, ntiles8;   // 128-row / 128-column tiles (ntiles8: rounded up to 8)
+    uint64_t *part;             // [M, ntiles] (value, ~id) max-keys per row and column tile
+    ArgMax *rowres;             // [M] published row results
+    int32_t *out_argmax;        // [M] or null
+    float *out_maxlogit;        // [M] or null
+};
+constexpr int kLmTile = 128;
+hipError_t launch_lmhead(const LmheadArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Sampling

@@ -35,6 +35,8 @@ Workloads (sizes are parameters; the defaults are the full sizes):
                  branch (the SSD fan-out lookup).
   trim           2^24 token ids over Vt=128256 from a bounded Zipf law (s = 1.1) at
                  random ids, P = 0.95 (the vocabulary trim; no corpus is used).
+  lmhead         hidden [128, 7, 4096] and W [128256, 4096] bfloat16 with a planted
+                 token per row (the fused lm_head -> greedy verification).
 """
 from __future__ import annotations
 
@@ -192,6 +194,52 @@ def token_stream(seed: int, N: int = 1 << 24, Vt: int = 128256, s: float = 1.1, 
     return dict(kind="trim", tokens=ids, Vt=Vt, P=0.95)
 
 
+def _bf16_rows(rng, shape, scale, block=1 << 22):
+    """Normal(0, scale^2) bfloat16 bits of the given 2-D shape, made in row
+    blocks of about `block` elements (bounded host memory)."""
+    rows, cols = shape
+    out = np.empty(shape, np.uint16)
+    step = max(1, block // max(cols, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        out[r0:r1] = bf16_bits(_normal(rng, (r1 - r0, cols), scale))
+    return out
+
+
+def lmhead(seed: int, B: int = 128, R: int = 7, d: int = 4096, V: int = 128256, alpha: float = 4.2,
+           noise: float = 0.8, p_match: float = 0.7, tree: bool = False, max_depth: int = 5,
+           max_children: int = 8) -> dict:
+    """Fused lm_head input: W [V, d] ~ N(0, 2.5^2 / d) and, for every row, a
+    planted token g whose unit weight row the hidden state follows:
+    h = alpha u_g + N(0, noise^2) per component (so g's logit is about
+    2.5 alpha, the others about N(0, (2.5 noise)^2)).  Chain: draft token i is
+    g of row i with probability p_match, else another id.  Tree (R = N nodes):
+    a random parent array and node token = g of the parent's row with
+    probability p_match.  All bfloat16; the defaults are a Llama-3-8B-sized
+    lm_head (d = 4096, V = 128256) over the greedy batch (B = 128, gamma = 6)."""
+    rng = np.random.default_rng(seed)
+    W = _bf16_rows(rng, (V, d), 2.5 / np.sqrt(d))
+    g = rng.integers(0, V, (B, R)).astype(np.int32)
+    Wg = bf16_to_f32(W[g.reshape(-1)]).astype(np.float64)
+    u = Wg / np.maximum(np.linalg.norm(Wg, axis=1, keepdims=True), 1e-30)
+    h = (alpha * u + rng.standard_normal(u.shape) * noise).astype(np.float32)
+    hidden = bf16_bits(h).reshape(B, R, d)
+    w = dict(kind="lmhead", hidden=hidden, W=W, planted=g, tree=tree)
+    if not tree:
+        gam = R - 1
+        match = rng.random((B, gam)) < p_match
+        w["tokens"] = np.where(match, g[:, :gam], _other_id(rng, V, g[:, :gam])).astype(np.int32)
+    else:
+        parents = np.stack([tree_topology(rng, R, max_depth, max_children) for _ in range(B)])
+        tokens = np.zeros((B, R), np.int32)
+        for b in range(B):
+            for k in range(1, R):
+                pg = g[b, parents[b, k]]
+                tokens[b, k] = pg if rng.random() < p_match else _other_id(rng, V, pg)
+        w["tokens"], w["parents"] = tokens, parents
+    return w
+
+
 def tree_topology(rng: np.random.Generator, N: int = 32, max_depth: int = 5, max_children: int = 8):
     """Random parent array: node 0 is the root; node k picks a parent uniformly
     among earlier nodes with depth < max_depth and fewer than max_children children."""
@@ -230,4 +278,5 @@ WORKLOADS = {
     "draft": draft,
     "fanout": fanout,
     "trim": token_stream,
+    "lmhead": lmhead,
 }

@@ -300,6 +300,41 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Fused lm_head -> greedy verification (SSD guide sec. 6: compute_logits turns
+ * the target's hidden states into logits; sec. 7: temperature-0 runs; the
+ * 2.16x EAGLE blog sec. 6 ties the cost of this classification matmul to the
+ * vocabulary).  logits[m][v] = sum_k hidden[m][k] * W[v][k] with bfloat16
+ * inputs and float32 accumulation on the matrix cores; only each row's
+ * argmax (largest logit, lowest id on ties) is kept -- the logits are never
+ * written -- and the greedy chain (spec_verify_greedy) or tree walk
+ * (spec_verify_tree_greedy) follows on those argmaxes.
+ *   hidden        [B, R, d] bfloat16 (R = gamma + 1 for the chain, N for the
+ *                 tree), 16-byte aligned, d a multiple of 8.
+ *   W             [V, d] bfloat16, 16-byte aligned.
+ *   out_argmax    [B * R] int32 or NULL: each row's argmax id.
+ *   out_maxlogit  [B * R] float32 or NULL: each row's largest logit.
+ *   The other arguments and outputs are those of spec_verify_greedy /
+ *   spec_verify_tree_greedy.
+ *   workspace     >= sv_workspace_bytes_lmhead(B * R, V) bytes.
+ * Float32 accumulation can order two logits that are within its rounding
+ * differently from exact arithmetic; such near-ties are the only way the
+ * argmax can differ from that of exact logits.
+ * Errors: SV_ERR_INVALID_ARG (null required pointer, B < 0, R < 1, d not a
+ * positive multiple of 8, misaligned hidden or W, V < 1), SV_ERR_TOO_LARGE,
+ * SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP.
+ */
+size_t sv_workspace_bytes_lmhead(int32_t M, int32_t V);
+sv_status spec_lmhead_verify_greedy(const void *hidden, const void *W, const int32_t *draft_tokens, int32_t B,
+                                    int32_t gamma, int32_t d, int32_t V, int32_t *out_tokens, int32_t *out_accept_len,
+                                    int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+sv_status spec_lmhead_verify_tree(const void *hidden, const void *W, const int32_t *node_tokens,
+                                  const int32_t *parents, int32_t B, int32_t N, int32_t d, int32_t V,
+                                  int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
+                                  int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sampling verification without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Arguments, outputs and results are those

@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "spec_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FLOAT32, BFLOAT16 = 0, 1
+FLOAT32, BFLOAT16, FLOAT64 = 0, 1, 2
 
 ST_TOKEN_RANGE, ST_D2T, ST_NO_MASS, ST_BAD_PARENT = 1, 2, 4, 8
 FL_ACCEPT_EDGE, FL_CDF_EDGE, FL_ZERO_RESID = 1, 2, 4
@@ -56,6 +56,8 @@ def _load():
         lib.oracle_count.argtypes = [P, i32, i32, P]
         lib.oracle_fanout_lookup.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P]
         lib.oracle_vocab_trim.argtypes = [P, C.c_int64, i32, f64, P, P, P, P]
+        lib.oracle_greedy_from_argmax.argtypes = [P, P, i32, i32, i32, P, P, P]
+        lib.oracle_tree_from_argmax.argtypes = [P, P, P, i32, i32, i32, P, P, P, P]
         lib.oracle_chain_from_dists.argtypes = [P, P, P, P, C.c_float, i32, i32, C.c_double, P, P]
         lib.oracle_verify_greedy.argtypes = [P, i32, P, i32, i32, i32, P, P, P]
         lib.oracle_verify_tree_greedy.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, P]
@@ -74,7 +76,9 @@ def _logits(a):
         return a, FLOAT32
     if a.dtype == np.uint16:
         return a, BFLOAT16
-    raise TypeError("logits must be float32 or uint16 (bfloat16 bits), got %s" % a.dtype)
+    if a.dtype == np.float64:
+        return a, FLOAT64
+    raise TypeError("logits must be float32, float64 or uint16 (bfloat16 bits), got %s" % a.dtype)
 
 
 def verify_sample(target_logits, draft_logits, tokens, u_accept, u_sample, temperature, top_p,
@@ -216,6 +220,60 @@ def vocab_trim(tokens, Vt, P):
     if rc != 0:
         raise ValueError("oracle_vocab_trim: bad arguments")
     return d2t[:vd[0]].copy(), t2d, info
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def lmhead_logits(hidden_bits, W_bits):
+    """D12: the lm_head's logits in float64: hidden [M, d] times W [V, d]^T from
+    bfloat16 bit patterns (widened exactly; numpy's float64 matmul), and the
+    same product of the absolute values, |hidden| |W|^T, which bounds the
+    rounding of any float32 accumulation of the same terms."""
+    h = _bf16_to_f64(hidden_bits)
+    w = _bf16_to_f64(W_bits)
+    return h @ w.T, np.abs(h) @ np.abs(w).T
+
+
+def lmhead_admissible(z, zabs, eps):
+    """Per row of float64 logits z [M, V]: the argmax (lowest id on ties) and
+    a boolean mask of the ids a float32 accumulation with relative error
+    eps (of |h||w|) may also report as the maximum: z_v >= z_max -
+    eps (zabs_v + zabs_max)."""
+    g = np.argmax(z, axis=1)
+    rows = np.arange(z.shape[0])
+    zm = z[rows, g]
+    am = zabs[rows, g]
+    return g.astype(np.int32), z >= zm[:, None] - eps * (zabs + am[:, None])
+
+
+def greedy_from_argmax(g, tokens, V):
+    """D7's chain on given row argmaxes g [B, g+1]."""
+    gg = np.ascontiguousarray(g, dtype=np.int32)
+    B, g1 = gg.shape
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, g1 - 1)
+    out = dict(tokens=np.empty((B, g1), np.int32), accept_len=np.empty(B, np.int32), status=np.empty(B, np.int32))
+    rc = _load().oracle_greedy_from_argmax(_ptr(gg), _ptr(tok), B, g1 - 1, int(V), _ptr(out["tokens"]),
+                                           _ptr(out["accept_len"]), _ptr(out["status"]))
+    if rc != 0:
+        raise ValueError("oracle_greedy_from_argmax: bad arguments")
+    return out
+
+
+def tree_from_argmax(g, node_tokens, parents, V):
+    """D8's walk on given row argmaxes g [B, N]."""
+    gg = np.ascontiguousarray(g, dtype=np.int32)
+    B, N = gg.shape
+    nt = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N)
+    pa = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, N)
+    out = dict(path=np.empty((B, N), np.int32), tokens=np.empty((B, N), np.int32),
+               accept_len=np.empty(B, np.int32), status=np.empty(B, np.int32))
+    rc = _load().oracle_tree_from_argmax(_ptr(gg), _ptr(nt), _ptr(pa), B, N, int(V), _ptr(out["path"]),
+                                         _ptr(out["tokens"]), _ptr(out["accept_len"]), _ptr(out["status"]))
+    if rc != 0:
+        raise ValueError("oracle_tree_from_argmax: bad arguments")
+    return out
 
 
 def verify_greedy(logits, tokens):

@@ -47,11 +47,15 @@
 #define ORC_EARG 1
 #define ORC_EMEM 2
 
-/* dtype codes of the raw logits: 0 = float32, 1 = bfloat16 bit patterns. */
+/* dtype codes of the raw logits: 0 = float32, 1 = bfloat16 bit patterns,
+ * 2 = float64 (logits the oracle computed itself, e.g. from an lm_head). */
 static double logit_at(const void *base, int dtype, size_t i)
 {
     if (dtype == 0) {
         return (double)((const float *)base)[i];
+    }
+    if (dtype == 2) {
+        return ((const double *)base)[i];
     }
     /* bfloat16 is the high half of a float32: widening is exact. */
     uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
@@ -717,6 +721,34 @@ static int32_t row_argmax(const void *base, int dtype, size_t off, int V, int *n
  * logits [B, gamma+1, V]; tokens [B, gamma]; out_tokens [B, gamma+1] (-1
  * padded); out_len [B]; out_status [B] or NULL.
  */
+/*
+ * D7's chain on given row argmaxes g [B, gamma+1] (the fused lm_head path
+ * reports its argmaxes; the chain rule is the same): n = first i with
+ * x_i != g_i, emit x_0..x_{n-1}, g_n.  status gets ORC_ST_TOKEN_RANGE for a
+ * token outside [0, V).
+ */
+int oracle_greedy_from_argmax(const int32_t *g, const int32_t *tokens, int B, int gamma, int V,
+                              int32_t *out_tokens, int32_t *out_len, int32_t *out_status)
+{
+    if (B < 0 || gamma < 0 || V < 1) return ORC_EARG;
+    for (int b = 0; b < B; ++b) {
+        int32_t st = 0;
+        int n = gamma;
+        for (int i = 0; i < gamma; ++i) {
+            int32_t x = tokens[(size_t)b * gamma + i];
+            if (x < 0 || x >= V) st |= ORC_ST_TOKEN_RANGE;
+            if (n == gamma && x != g[(size_t)b * (gamma + 1) + i]) n = i;
+        }
+        int32_t *ot = out_tokens + (size_t)b * (gamma + 1);
+        for (int i = 0; i <= gamma; ++i) ot[i] = -1;
+        for (int i = 0; i < n; ++i) ot[i] = tokens[(size_t)b * gamma + i];
+        ot[n] = g[(size_t)b * (gamma + 1) + n];
+        out_len[b] = n;
+        if (out_status) out_status[b] = st;
+    }
+    return ORC_OK;
+}
+
 int oracle_verify_greedy(const void *logits, int dtype, const int32_t *tokens,
                          int B, int gamma, int V, int32_t *out_tokens,
                          int32_t *out_len, int32_t *out_status)
@@ -764,6 +796,55 @@ int oracle_verify_greedy(const void *logits, int dtype, const int32_t *tokens,
  * of the path (-1 padded); out_tokens [B, N] (path tokens then the bonus, -1
  * padded); out_len [B] = depth of best; out_status [B] or NULL.
  */
+/*
+ * D8's walk on given row argmaxes g [B, N] (as reported by the fused lm_head
+ * path): the same acceptance rule, winner and outputs as
+ * oracle_verify_tree_greedy, without the no-mass check (g carries no values).
+ */
+int oracle_tree_from_argmax(const int32_t *gall, const int32_t *node_tokens, const int32_t *parents,
+                            int B, int N, int V, int32_t *out_path, int32_t *out_tokens,
+                            int32_t *out_len, int32_t *out_status)
+{
+    if (B < 0 || N < 1 || V < 1) return ORC_EARG;
+    int32_t *depth = malloc(sizeof(int32_t) * (size_t)N);
+    unsigned char *acc = malloc((size_t)N);
+    int32_t *stack = malloc(sizeof(int32_t) * (size_t)N);
+    if (!depth || !acc || !stack) { free(depth); free(acc); free(stack); return ORC_EMEM; }
+    for (int b = 0; b < B; ++b) {
+        const int32_t *g = gall + (size_t)b * N;
+        int32_t st = 0;
+        acc[0] = 1;
+        depth[0] = 0;
+        for (int k = 1; k < N; ++k) {
+            int32_t pk = parents[(size_t)b * N + k];
+            int32_t tk = node_tokens[(size_t)b * N + k];
+            acc[k] = 0;
+            depth[k] = 0;
+            if (tk < 0 || tk >= V) st |= ORC_ST_TOKEN_RANGE;
+            if (pk < 0 || pk >= k) { st |= ORC_ST_BAD_PARENT; continue; }
+            depth[k] = depth[pk] + 1;
+            acc[k] = acc[pk] && tk == g[pk];
+        }
+        int best = 0;
+        for (int k = 1; k < N; ++k)
+            if (acc[k] && depth[k] > depth[best]) best = k;
+        int d = 0;
+        for (int k = best; k != 0; k = parents[(size_t)b * N + k]) stack[d++] = k;
+        int32_t *op = out_path + (size_t)b * N;
+        int32_t *ot = out_tokens + (size_t)b * N;
+        for (int k = 0; k < N; ++k) { op[k] = -1; ot[k] = -1; }
+        for (int s2 = 0; s2 < d; ++s2) {
+            op[s2] = stack[d - 1 - s2];
+            ot[s2] = node_tokens[(size_t)b * N + op[s2]];
+        }
+        ot[d] = g[best];
+        out_len[b] = d;
+        if (out_status) out_status[b] = st;
+    }
+    free(depth); free(acc); free(stack);
+    return ORC_OK;
+}
+
 int oracle_verify_tree_greedy(const void *logits, int dtype, const int32_t *node_tokens,
                               const int32_t *parents, int B, int N, int V,
                               int32_t *out_path, int32_t *out_tokens, int32_t *out_len,

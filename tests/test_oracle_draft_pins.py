@@ -294,3 +294,58 @@ def test_vocab_trim_feeds_verification(oracle_mod):
     out = oracle_mod.verify_sample(zt, zd, d2t[rng.integers(0, Vd, (2, 2))], synth.uniforms(rng, (2, 2)),
                                    synth.uniforms(rng, (2,)), 1.0, 1.0, d2t=d2t)
     assert (out["status"] & oracle_mod.ST_D2T == 0).all()
+
+
+# --------------------------------------------------------------------------
+# The lm_head in float64 and the greedy rules on given argmaxes (SSD guide
+# sec. 6 compute_logits, sec. 7 temperature 0; EAGLE blog sec. 5 tree)
+# --------------------------------------------------------------------------
+
+def test_lmhead_logits_brute_force(oracle_mod):
+    rng = np.random.default_rng(914)
+    M, V, d = 3, 5, 8
+    h = synth.bf16_bits(rng.standard_normal((M, d)).astype(np.float32))
+    w = synth.bf16_bits(rng.standard_normal((V, d)).astype(np.float32))
+    z, za = oracle_mod.lmhead_logits(h, w)
+    hf, wf = synth.bf16_to_f32(h), synth.bf16_to_f32(w)
+    for m in range(M):
+        for v in range(V):
+            assert z[m, v] == sum(float(hf[m, k]) * float(wf[v, k]) for k in range(d))
+            assert za[m, v] == sum(abs(float(hf[m, k]) * float(wf[v, k])) for k in range(d))
+
+
+def test_lmhead_one_hot_rows_pick_columns(oracle_mod):
+    """A one-hot hidden row e_k reads column k of W: its logits are W[:, k]."""
+    rng = np.random.default_rng(915)
+    V, d = 300, 16
+    w = synth.bf16_bits(rng.standard_normal((V, d)).astype(np.float32))
+    h = synth.bf16_bits(np.eye(d, dtype=np.float32))
+    z, _ = oracle_mod.lmhead_logits(h, w)
+    np.testing.assert_array_equal(z, synth.bf16_to_f32(w).T.astype(np.float64))
+
+
+def test_greedy_and_tree_from_argmax_match_logit_forms(oracle_mod):
+    rng = np.random.default_rng(916)
+    B, g, V = 30, 5, 40
+    z = rng.integers(-3, 4, (B, g + 1, V)).astype(np.float64)          # ties included
+    am = np.argmax(z, axis=-1).astype(np.int32)
+    tok = np.where(rng.random((B, g)) < 0.6, am[:, :g], rng.integers(0, V, (B, g))).astype(np.int32)
+    a = oracle_mod.verify_greedy(z, tok)
+    b = oracle_mod.greedy_from_argmax(am, tok, V)
+    for k in ("tokens", "accept_len", "status"):
+        np.testing.assert_array_equal(a[k], b[k])
+    t = synth.tree(917, B=6, N=20, V=40)
+    zt = rng.integers(-3, 4, (6, 20, 40)).astype(np.float64)
+    a = oracle_mod.verify_tree_greedy(zt, t["tokens"], t["parents"])
+    b = oracle_mod.tree_from_argmax(np.argmax(zt, axis=-1), t["tokens"], t["parents"], 40)
+    for k in ("path", "tokens", "accept_len", "status"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_lmhead_admissible_sets(oracle_mod):
+    z = np.array([[1.0, 3.0, 3.0 - 1e-9, 2.0], [5.0, 0.0, 5.0, 4.999]])
+    za = np.full_like(z, 100.0)
+    g, adm = oracle_mod.lmhead_admissible(z, za, 2.0 ** -18)          # band 2 * 100 * 2^-18 = 7.6e-4
+    assert g.tolist() == [1, 0]
+    assert adm[0].tolist() == [False, True, True, False]
+    assert adm[1].tolist() == [True, False, True, False]
