@@ -483,8 +483,10 @@ def main():
     line = dict(metric=METRIC, value=r["rows_per_s"], unit="rows/s", n_gpus=1, steps=K, warmup=args.warmup,
                 ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="f32", data="synthetic", config=cfg,
-                roofline=dict(bound="hbm", achieved=r["achieved_GBps"], peak=PEAK_GBS, unit="GB/s",
-                              frac=r["frac"], traffic=r["traffic"]),
+                roofline=(dict(bound="mfma", achieved=r["achieved_TFLOPs"], peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                               frac=r["mfma_frac"], traffic=r["traffic"]) if r.get("bound") == "mfma" else
+                          dict(bound="hbm", achieved=r["achieved_GBps"], peak=PEAK_GBS, unit="GB/s",
+                               frac=r["frac"], traffic=r["traffic"])),
                 cpu_baseline=cpu)
     print(json.dumps(line), flush=True)
 

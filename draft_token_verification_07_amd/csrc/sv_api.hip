@@ -387,7 +387,7 @@ sv_status run_lmhead(const void *hidden, const void *W, const int32_t *tokens, c
     L.V = V;
     L.mtiles = (int32_t)((M + kLmTile - 1) / kLmTile);
     L.ntiles = (int32_t)nt;
-    L.ntiles8 = (int32_t)((nt + 7) / 8 * 8);
+    L.ntiles8 = (int32_t)(((nt + 1) / 2 + 7) / 8 * 8);
     if (!grid_fits((int64_t)L.mtiles * L.ntiles8)) return SV_ERR_TOO_LARGE;
     char *data = static_cast<char *>(ws) + counter_region(ws_bytes);
     L.part = reinterpret_cast<uint64_t *>(data);

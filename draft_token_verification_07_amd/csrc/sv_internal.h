@@ -119,7 +119,7 @@ struct LmheadArgs {
     const uint16_t *hidden;     // [M, d] bfloat16 bits, M = B * R
     const uint16_t *W;          // [V, d] bfloat16 bits
     int32_t M, d, V;
-    int32_t mtiles, ntiles, ntiles8;   // 128-row / 128-column tiles (ntiles8: rounded up to 8)
+    int32_t mtiles, ntiles, ntiles8;   // 128-row / 128-column tiles; ntiles8: 256-column GEMM tiles rounded up to 8
     uint64_t *part;             // [M, ntiles] (value, ~id) max-keys per row and column tile
     ArgMax *rowres;             // [M] published row results
     int32_t *out_argmax;        // [M] or null
