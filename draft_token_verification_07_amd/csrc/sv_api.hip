@@ -353,11 +353,7 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
     a.out_vd = out_vd;
     a.out_info = out_info;
     char *base = static_cast<char *>(workspace);
-    char *data = base + counter_region(workspace_bytes);
-    a.S = trim_slices(Vt);
-    a.totals = reinterpret_cast<unsigned long long *>(base);
-    a.part = reinterpret_cast<uint32_t *>(data);
-    a.counts = reinterpret_cast<uint32_t *>(data + align256(sizeof(uint32_t) * (size_t)a.S * Vt));
+    trim_layout(a, base, base + counter_region(workspace_bytes));
     return launch_trim(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -249,6 +249,20 @@ hipError_t launch_fanout(const FanoutArgs &a, hipStream_t st);
 // ---------------------------------------------------------------------------
 // Vocabulary-trim d2t builder
 // ---------------------------------------------------------------------------
+// State of one call, written by the reduce and refine launches and read by
+// the later ones (data region).
+struct TrimState {
+    unsigned long long valid, invalid;   // tokens in [0, Vt) and outside it
+    unsigned long long aboveB;           // mass of the buckets above the boundary bucket
+    unsigned long long above;            // mass of the ids with count > cstar
+    double T;                            // P * valid
+    int32_t mode;                        // 0: nothing kept, 1: every nonzero id, 2: a cut
+    int32_t refine;                      // 0: cstar known, 1: exact histogram, 2: sorted list
+    uint32_t lo, hi;                     // count range of the boundary bucket
+    uint32_t nB;                         // ids in the boundary bucket
+    uint32_t cstar, take;                // the cut: ids of count > cstar, and the take lowest of cstar
+    uint32_t list_n;                     // entries of the list (refine 2)
+};
 struct TrimArgs {
     const int32_t *tokens;        // [N]
     int64_t N;
@@ -259,17 +273,31 @@ struct TrimArgs {
     int32_t *out_vd;              // [1]
     int64_t *out_info;            // [3] or null: kept mass, valid tokens, invalid tokens
     int32_t S;                    // stream slices
-    uint32_t *part;               // [S, Vt] partial histograms
+    int32_t R, logR, KB;          // id ranges (ids t with t % R == r), bins per range (a multiple of 4)
+    int32_t nblocks;              // 1024-id blocks of the output pass
+    uint32_t *part;               // [S, R, KB] partial histograms
     uint32_t *counts;             // [Vt]
+    uint32_t *hist_n;             // [kTrimBuckets] ids per count bucket
+    unsigned long long *hist_m;   // [kTrimBuckets] their count sum
+    uint32_t *h2;                 // [kTrimFine] ids per exact count inside the boundary bucket
+    uint32_t *list;               // [kTrimList] counts inside the boundary bucket (wide buckets)
+    uint32_t *blockdef, *blocktie;  // [nblocks] ids above the cut / on it, per block
+    TrimState *state;
     unsigned long long *totals;   // [2] valid, invalid (counter region; returned to zero)
+    uint32_t *arrive;             // [2] arrival counters (counter region; returned to zero)
 };
-constexpr int kTrimBins = 16384;        // ids per partial-histogram workgroup (64 KiB of LDS)
+constexpr int kTrimBins = 32768;        // bins per partial-histogram workgroup (128 KiB of LDS)
 constexpr int kTrimTargetWgs = 256;     // ranges x slices
 constexpr int kTrimMaxSlices = 64;
-int32_t trim_ranges(int32_t Vt);
-int32_t trim_slices(int32_t Vt);
+constexpr int kTrimBuckets = 1728;      // count buckets: exact below 128, then 64 per octave
+constexpr int kTrimFine = 4096;         // widest boundary bucket refined by an exact histogram
+constexpr int kTrimList = 4096;         // most ids in a wider boundary bucket
+constexpr int kTrimBlock = 1024;        // ids per block of the output pass
 size_t trim_counter_bytes(int32_t Vt);
 size_t trim_data_bytes(int32_t Vt);
+// Fills the size fields and workspace pointers of a (counter region at
+// base, data region at data).
+void trim_layout(TrimArgs &a, char *base, char *data);
 hipError_t launch_trim(const TrimArgs &a, hipStream_t st);
 
 // Workspace of W bytes: [0, K) holds the arrival counters, [K, W) the data,

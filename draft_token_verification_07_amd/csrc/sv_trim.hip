@@ -9,19 +9,29 @@
 // are.  d2t lists the kept ids in ascending order (the map verification
 // takes) and t2d is its inverse.
 //
-// Three launches:
-//   trim_part_kernel: workgroup (r, s) counts the ids of range r (kTrimBins
-//     ids, an LDS histogram) in slice s of the stream and stores the partial
-//     histogram, coalesced.  The workgroups of one slice run on one XCD (the
-//     block order puts them kTrimSlices apart), so the slice is read from HBM
-//     once and from that XCD's L2 by the other ranges.  No global atomics.
-//   trim_reduce_kernel: sums the partial histograms of every id.
-//   trim_select_kernel: one workgroup selects the cut exactly in integers: a
-//     radix select over the 32-bit counts (8-bit digits, count and mass
-//     histograms in LDS, each wave adding its most common digit at once)
-//     finds the count c* at which the mass from the top reaches P * N and how
-//     many ids of count c* are needed, the lowest ids on c* are taken, and a
-//     scan over the ids writes d2t and t2d.
+// The kept set is {count > c*} plus the lowest `take` ids of count c*, where
+// c* is the largest count whose mass from the top (the count sum of the ids
+// of count >= c*) reaches T = P * valid.  Five launches, every one spread
+// over the chip; each launch boundary is the only synchronisation, except
+// where the last workgroup to arrive on a counter finishes a step:
+//   trim_part_kernel: workgroup (r, s) counts the ids t with t % R == r (an
+//     LDS histogram of ceil(Vt / R) bins) in slice s of the stream and stores
+//     the partial histogram.  Ranges by residue spread the frequent ids of a
+//     skewed corpus over all ranges.  When S is a multiple of 8 the
+//     workgroups of one slice run on one XCD (the block order puts them S
+//     apart), so the slice is read from HBM once.  No global atomics.
+//   trim_reduce_kernel: sums the partial histograms of every id, and adds
+//     every id to a histogram of count buckets (exact below 128, then 64 per
+//     octave; count and mass).  The last workgroup finds the bucket holding
+//     c*: the first from the top whose mass brings the total to T.
+//   trim_refine_kernel: when that bucket spans several counts, the ids in it
+//     give an exact histogram of their counts (buckets up to kTrimFine wide)
+//     or a list of them (wider buckets hold counts >= 2^19, so at most
+//     2^31 / 2^19 ids), and the last workgroup finds c* and take.
+//   trim_count_kernel: per block of kTrimBlock ids, the ids above the cut
+//     and on it.
+//   trim_write_kernel: every block ranks its kept ids from the block counts
+//     before it and writes d2t and t2d; the last block writes the totals.
 #include <math.h>
 
 #include "sv_common.h"
@@ -30,321 +40,618 @@
 
 namespace sv {
 
-constexpr int kTrimPartThreads = 512;
-constexpr int kTrimPartUnroll = 8;        // 16-byte vectors in flight per thread
-constexpr int kTrimSelThreads = 512;
-constexpr int kTrimSelUnroll = 8;         // counts in flight per thread
-constexpr int kTrimDigitBits = 11;        // radix digits: 11 + 11 + 10 bits
-constexpr int kTrimDigits = 1 << kTrimDigitBits;
+constexpr int kTrimPartThreads = 1024;    // one workgroup per CU (its LDS histogram takes 128 KiB)
+constexpr int kTrimPartUnroll = 4;        // 16-byte vectors per round (two rounds in flight)
+constexpr int kTrimThreads = 256;         // the other launches
 
-// Workgroup (r, s): the ids of range r in slice s of the stream.  The stream
-// is read as 16-byte vectors (4 ids), kTrimPartUnroll per thread in flight;
-// the ids before the first 16-byte boundary go to slice 0, those after the
-// last full vector to the last slice.
+// Count bucket of c >= 1: c itself below 128; above, 64 buckets per octave
+// [2^e, 2^(e+1)), e = 7..31, by the six bits below the leading one.  The
+// bucket index grows with c.
+__device__ __forceinline__ int trim_bucket(uint32_t c) {
+    if (c < 128u) return (int)c;
+    const int e = 31 - __clz(c);
+    return 128 + (e - 7) * 64 + (int)((c >> (e - 6)) & 63u);
+}
+__device__ __forceinline__ void trim_bucket_range(int B, uint32_t *lo, uint32_t *hi) {
+    if (B < 128) {
+        *lo = *hi = (uint32_t)B;
+        return;
+    }
+    const int e = 7 + (B - 128) / 64, sub = (B - 128) % 64;
+    const uint64_t l = (uint64_t)(64 + sub) << (e - 6);
+    *lo = (uint32_t)l;
+    *hi = (uint32_t)(l + ((uint64_t)1 << (e - 6)) - 1u);
+}
+
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_agent_u64(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Adds (number of lanes, sum of val) to `key` for every lane with `in` set:
+// the lanes on the leader's key at once (twice), then the rest one by one,
+// since most lanes of a skewed input share a few keys and per-lane atomics on
+// one address serialise.  Called by every lane of the wave.
+template <bool VAL, typename F>
+__device__ __forceinline__ void wave_aggregate(bool in, int key, uint64_t val, F &&add) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+        const uint64_t act = __ballot(in);
+        if (!act) return;
+        const int leader = __ffsll((unsigned long long)act) - 1;
+        const int kl = __shfl(key, leader, kWave);
+        const bool mine = in && key == kl;
+        const uint64_t m = __ballot(mine);
+        uint64_t tot = 0;
+        if constexpr (VAL) tot = wave_total_u64(mine ? val : 0ull);
+        if (lane == leader) add(kl, (uint32_t)__popcll(m), tot);
+        in = in && !mine;
+    }
+    if (in) add(key, 1u, val);
+}
+
+// Exclusive scan of v over the workgroup in thread order; *total gets the sum.
+template <int NT>
+__device__ __forceinline__ uint64_t wg_excl_scan_u64(uint64_t v, uint64_t *s_tmp, uint64_t *total) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const uint64_t inc = wave_incl_scan_u64_dpp(v);
+    if (lane == kWave - 1) s_tmp[wv] = inc;
+    __syncthreads();
+    uint64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint64_t x = s_tmp[w];
+        if (w < wv) before += x;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - v;
+}
+
+__device__ __forceinline__ uint32_t trim_take(double T, unsigned long long above, uint32_t cs) {
+    // the fewest ids of count cs that bring the mass to T (the mass above cs
+    // is below T, and all of cs's ids reach it)
+    const double need = ceil((T - (double)above) / (double)cs);
+    uint32_t take = need < 1.0 ? 1u : (uint32_t)need;
+    while (take > 1 && (double)(above + (unsigned long long)(take - 1) * cs) >= T) --take;
+    while ((double)(above + (unsigned long long)take * cs) < T) ++take;
+    return take;
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: partial histograms
+// ---------------------------------------------------------------------------
 template <int NT, int U>
 __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
     __shared__ uint32_t s_h[kTrimBins];
     __shared__ uint32_t s_inv;
     const int32_t r = blockIdx.x / a.S, sl = blockIdx.x % a.S;
-    const int32_t id0 = r * kTrimBins;
-    const int32_t nb = min(kTrimBins, a.Vt - id0);
-    for (int k = threadIdx.x; k < kTrimBins; k += NT) s_h[k] = 0;
+    const int32_t Rm = a.R - 1, logR = a.logR;
+    const uint32_t Vt = (uint32_t)a.Vt;
+    for (int k = threadIdx.x; k < a.KB; k += NT) s_h[k] = 0;
     if (threadIdx.x == 0) s_inv = 0;
+    // what the later launches accumulate into starts at zero
+    {
+        const int32_t gsz = (int32_t)gridDim.x * NT, gi = (int32_t)blockIdx.x * NT + (int32_t)threadIdx.x;
+        for (int32_t k = gi; k < kTrimBuckets; k += gsz) {
+            a.hist_n[k] = 0;
+            a.hist_m[k] = 0;
+        }
+        for (int32_t k = gi; k < kTrimFine; k += gsz) a.h2[k] = 0;
+    }
     __syncthreads();
     uint32_t invalid = 0;
-    auto one = [&](int32_t t) {
-        const int32_t k = t - id0;
-        if ((uint32_t)k < (uint32_t)nb) atomicAdd(&s_h[k], 1u);
-        else if (r == 0 && (t < 0 || t >= a.Vt)) ++invalid;          // counted once, by range 0
+    // ok: the token is real
+    auto one = [&](int32_t t, bool ok) {
+        const bool inr = (uint32_t)t < Vt;
+        if (ok && inr && (t & Rm) == r) atomicAdd(&s_h[t >> logR], 1u);
+        if (r == 0 && ok && !inr) ++invalid;                  // counted once, by range 0
     };
     const uintptr_t base = reinterpret_cast<uintptr_t>(a.tokens);
     int64_t head = (int64_t)(((16u - (uint32_t)(base & 15u)) & 15u) / 4u);
     if (head > a.N) head = a.N;
     const int64_t nvec = (a.N - head) / 4;
     const int64_t tail0 = head + nvec * 4;
-    if (sl == 0 && (int64_t)threadIdx.x < head) one(a.tokens[threadIdx.x]);
-    if (sl == a.S - 1 && (int64_t)threadIdx.x < a.N - tail0) one(a.tokens[tail0 + threadIdx.x]);
+    {
+        const bool h = sl == 0 && (int64_t)threadIdx.x < head;
+        one(h ? a.tokens[threadIdx.x] : 0, h);
+        const bool tl = sl == a.S - 1 && (int64_t)threadIdx.x < a.N - tail0;
+        one(tl ? a.tokens[tail0 + threadIdx.x] : 0, tl);
+    }
     const u32x4 *body = reinterpret_cast<const u32x4 *>(a.tokens + head);
     const int64_t v0 = nvec * sl / a.S, v1 = nvec * (sl + 1) / a.S;
-    for (int64_t v = v0 + threadIdx.x; v < v1; v += (int64_t)U * NT) {
-        u32x4 raw[U];
+    // rounds of U * NT vectors; the next round's loads are issued before
+    // this round's ids are counted (clamped indices past the slice)
+    if (v1 > v0) {
+        auto load = [&](int64_t vb, u32x4 (&raw)[U]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t j = v + (int64_t)u * NT;
-            raw[u] = __builtin_nontemporal_load(&body[j < v1 ? j : v1 - 1]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (v + (int64_t)u * NT < v1) {
-                one((int32_t)raw[u].x);
-                one((int32_t)raw[u].y);
-                one((int32_t)raw[u].z);
-                one((int32_t)raw[u].w);
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = vb + (int64_t)u * NT + threadIdx.x;
+                raw[u] = __builtin_nontemporal_load(&body[j < v1 ? j : v1 - 1]);
             }
+        };
+        u32x4 cur[U], nxt[U];
+        load(v0, cur);
+        for (int64_t vb = v0; vb < v1; vb += (int64_t)U * NT) {
+            if (vb + (int64_t)U * NT < v1) load(vb + (int64_t)U * NT, nxt);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = vb + (int64_t)u * NT + threadIdx.x < v1;
+                one((int32_t)cur[u].x, ok);
+                one((int32_t)cur[u].y, ok);
+                one((int32_t)cur[u].z, ok);
+                one((int32_t)cur[u].w, ok);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
     }
     if (r == 0 && invalid) atomicAdd(&s_inv, invalid);
     __syncthreads();
-    uint32_t *dst = a.part + (size_t)sl * a.Vt + id0;
-    for (int k = threadIdx.x; k < nb; k += NT) dst[k] = s_h[k];
+    uint32_t *dst = a.part + ((size_t)sl * a.R + r) * a.KB;
+    for (int k = threadIdx.x; k < a.KB; k += NT) dst[k] = s_h[k];
     if (r == 0 && threadIdx.x == 0 && s_inv) atomicAdd(&a.totals[1], (unsigned long long)s_inv);
 }
 
-// counts[t] = sum over the slices of the partial counts of t (eight loads in
-// flight per thread); the total goes to totals[0] (one atomic per workgroup)
+// ---------------------------------------------------------------------------
+// Launch 2: counts, the count-bucket histogram, the boundary bucket
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ void trim_boundary(const TrimArgs &a) {
+    constexpr int PER = (kTrimBuckets + NT - 1) / NT;
+    __shared__ unsigned long long s_tot[2];
+    __shared__ uint64_t s_tmp[NT / kWave];
+    __shared__ int s_B;
+    __shared__ unsigned long long s_aboveB;
+    if (threadIdx.x == 0) {
+        s_tot[0] = ld_agent_u64(&a.totals[0]);
+        s_tot[1] = ld_agent_u64(&a.totals[1]);
+        // the counter region goes back to zero (read by this workgroup only)
+        __hip_atomic_store(&a.totals[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.totals[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_B = -1;
+        s_aboveB = 0;
+    }
+    __syncthreads();
+    const unsigned long long valid = s_tot[0], invalid = s_tot[1];
+    const double T = (double)a.P * (double)valid;
+    const int mode = valid == 0 ? 0 : (T >= (double)valid ? 1 : 2);
+    if (mode == 2) {
+        // thread i takes buckets [top - PER (i + 1), top - PER i): chunk sums,
+        // the mass above each chunk, then the crossing chunk walks its buckets
+        const int hiB = kTrimBuckets - 1 - PER * (int)threadIdx.x;
+        uint64_t m = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int b = hiB - q;
+            if (b >= 0) m += ld_agent_u64(&a.hist_m[b]);
+        }
+        uint64_t all;
+        const uint64_t before = wg_excl_scan_u64<NT>(m, s_tmp, &all);
+        if ((double)before < T && (double)(before + m) >= T) {
+            unsigned long long acc = before;
+            for (int q = 0; q < PER; ++q) {
+                const int b = hiB - q;
+                if (b < 0) break;
+                const unsigned long long mb = ld_agent_u64(&a.hist_m[b]);
+                if (mb == 0) continue;
+                if ((double)(acc + mb) >= T) {
+                    s_B = b;
+                    s_aboveB = acc;
+                    break;
+                }
+                acc += mb;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        TrimState st;
+        st.valid = valid;
+        st.invalid = invalid;
+        st.T = T;
+        st.mode = mode;
+        st.aboveB = 0;
+        st.above = 0;
+        st.refine = 0;
+        st.lo = st.hi = 1;
+        st.nB = 0;
+        st.cstar = 1;
+        st.take = 0;
+        st.list_n = 0;
+        const int B = s_B;
+        if (mode == 2 && B >= 0) {
+            uint32_t lo, hi;
+            trim_bucket_range(B, &lo, &hi);
+            st.lo = lo;
+            st.hi = hi;
+            st.aboveB = s_aboveB;
+            st.nB = ld_agent_u32(&a.hist_n[B]);
+            if (lo == hi) {
+                st.cstar = lo;
+                st.above = s_aboveB;
+                st.take = trim_take(T, s_aboveB, lo);
+            } else {
+                st.refine = (uint64_t)hi - lo + 1 <= (uint64_t)kTrimFine ? 1 : 2;
+            }
+        }
+        *a.state = st;
+    }
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
     constexpr int NW = NT / kWave;
     __shared__ uint64_t s_w[NW];
-    const int32_t t = blockIdx.x * NT + threadIdx.x;
-    uint32_t c = 0;
-    if (t < a.Vt) {
-        int32_t sl = 0;
-        for (; sl + 8 <= a.S; sl += 8) {
-            uint32_t p[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) p[u] = a.part[(size_t)(sl + u) * a.Vt + t];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) c += p[u];
-        }
-        for (; sl < a.S; ++sl) c += a.part[(size_t)sl * a.Vt + t];
-        a.counts[t] = c;
+    __shared__ int s_last;
+    __shared__ uint32_t s_hn[kTrimBuckets];
+    __shared__ unsigned long long s_hm[kTrimBuckets];
+    for (int b = threadIdx.x; b < kTrimBuckets; b += NT) {
+        s_hn[b] = 0;
+        s_hm[b] = 0;
     }
-    const uint64_t tot = wave_total_u64((uint64_t)c);
+    __syncthreads();
+    // thread: bins k0..k0+3 of range r (one 16-byte load per slice; rows of
+    // KB bins, KB a multiple of 4), i.e. ids (k0 + q) R + r
+    const int32_t i = (int32_t)blockIdx.x * NT + (int32_t)threadIdx.x;      // over [0, R * KB / 4)
+    const int32_t q4 = a.KB >> 2;
+    const int32_t r = i / q4, k0 = (i - r * q4) << 2;
+    const bool own = r < a.R;
+    u32x4 c4 = {0u, 0u, 0u, 0u};
+    if (own) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.part + (size_t)r * a.KB + k0);
+        const size_t stride = ((size_t)a.R * a.KB) >> 2;
+        int32_t sl = 0;
+        for (; sl + 16 <= a.S; sl += 16) {
+            u32x4 q[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) q[u] = p[(size_t)(sl + u) * stride];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                c4.x += q[u].x; c4.y += q[u].y; c4.z += q[u].z; c4.w += q[u].w;
+            }
+        }
+        for (; sl < a.S; ++sl) {
+            const u32x4 q = p[(size_t)sl * stride];
+            c4.x += q.x; c4.y += q.y; c4.z += q.z; c4.w += q.w;
+        }
+    }
+    // the workgroup's bucket histogram in LDS, then one global add per
+    // nonzero bucket (a bucket of small counts holds most ids of a skewed
+    // corpus, and per-id global atomics on it would serialise)
+    uint64_t csum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int32_t t = ((k0 + q) << a.logR) + r;
+        const uint32_t c = q == 0 ? c4.x : q == 1 ? c4.y : q == 2 ? c4.z : c4.w;
+        if (own && t < a.Vt) {
+            a.counts[t] = c;
+            csum += c;
+            if (c > 0) {
+                const int b = trim_bucket(c);
+                atomicAdd(&s_hn[b], 1u);
+                atomicAdd(&s_hm[b], (unsigned long long)c);
+            }
+        }
+    }
+    const uint64_t tot = wave_total_u64(csum);
     if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = tot;
     __syncthreads();
+    for (int b = threadIdx.x; b < kTrimBuckets; b += NT) {
+        const uint32_t n = s_hn[b];
+        if (n) {
+            atomicAdd(&a.hist_n[b], n);
+            atomicAdd(&a.hist_m[b], s_hm[b]);
+        }
+    }
     if (threadIdx.x == 0) {
         uint64_t m = 0;
         for (int w = 0; w < NW; ++w) m += s_w[w];
         if (m) atomicAdd(&a.totals[0], (unsigned long long)m);
     }
+    if (!arrive_last(&a.arrive[0], gridDim.x, &s_last)) return;
+    trim_boundary<NT>(a);
 }
 
-// One workgroup.  Every pass over the counts takes them in rounds of U * NT
-// ids, U loads per thread in flight, thread i of a round holding ids
-// base + u * NT + i (coalesced).  Ids are ranked in id order by ballots:
-// within a sub-round by the lanes below, across waves and sub-rounds by LDS
-// totals, across rounds by a running total.
-template <int NT, int U>
-__global__ __launch_bounds__(NT) void trim_select_kernel(TrimArgs a) {
-    constexpr int NW = NT / kWave;
-    __shared__ uint32_t s_n[kTrimDigits];
-    __shared__ unsigned long long s_mass[kTrimDigits];
-    __shared__ uint32_t s_prefix;
-    __shared__ unsigned long long s_above, s_mtot[NW];
-    __shared__ uint32_t s_cstar, s_take;
-    __shared__ int32_t s_tie, s_mode;     // mode 0: nothing kept, 1: every nonzero id, 2: the cut (c*, tie id)
-    __shared__ int32_t s_cnt[U][NW];
-    const int32_t Vt = a.Vt;
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    const unsigned long long valid = a.totals[0], invalid = a.totals[1];
-    const double T = (double)a.P * (double)valid;
+// ---------------------------------------------------------------------------
+// Launch 3: the exact cut inside the boundary bucket
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ void trim_cut(const TrimArgs &a, const TrimState &st) {
+    __shared__ uint64_t s_tmp[NT / kWave];
+    __shared__ uint32_t s_cs;
+    __shared__ unsigned long long s_above;
+    __shared__ uint64_t s_l[kTrimList];
+    const double T = st.T;
     if (threadIdx.x == 0) {
-        s_prefix = 0;
-        s_above = 0;
-        s_mode = valid == 0 ? 0 : (T >= (double)valid ? 1 : 2);
-        s_cstar = 1;
-        s_take = 0;
-        s_tie = -1;
+        s_cs = 0;
+        s_above = st.aboveB;
     }
     __syncthreads();
-    const int mode = s_mode;
-    auto load_round = [&](int32_t tb, uint32_t (&c)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t t = tb + u * NT + (int32_t)threadIdx.x;
-            c[u] = a.counts[t < Vt ? t : Vt - 1];
+    if (st.refine == 1) {
+        // exact histogram over [lo, hi]: thread i takes the values
+        // (hi - PER (i + 1), hi - PER i]
+        constexpr int PER = (kTrimFine + NT - 1) / NT;
+        const int64_t top = (int64_t)st.hi - (int64_t)PER * threadIdx.x;
+        uint64_t m = 0;
+        for (int q = 0; q < PER; ++q) {
+            const int64_t v = top - q;
+            if (v >= (int64_t)st.lo) m += (uint64_t)v * ld_agent_u32(&a.h2[v - st.lo]);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (tb + u * NT + (int32_t)threadIdx.x >= Vt) c[u] = 0u;
-    };
-    if (mode == 2) {
-        // the count c* at which the mass from the top reaches T, digit by
-        // digit (bits 31..21, 20..10, 9..0): the first bucket from the top
-        // whose mass brings the total to T
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const int bits = pass == 2 ? 10 : 11;
-            const int hi_shift = shift + bits;
-            for (int k = threadIdx.x; k < kTrimDigits; k += NT) { s_n[k] = 0; s_mass[k] = 0; }
-            __syncthreads();
-            const uint32_t pre = s_prefix;
-            for (int32_t tb = 0; tb < Vt; tb += U * NT) {
-                uint32_t cc[U];
-                load_round(tb, cc);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t c = cc[u];
-                    bool in = c != 0 && (pass == 0 || (c >> hi_shift) == (pre >> hi_shift));
-                    const uint32_t dig = (c >> shift) & ((1u << bits) - 1u);
-                    // each wave adds the ids on its leader's digit at once,
-                    // twice, then the rest one by one: most counts share
-                    // their high digits, and per-lane atomics on one bin
-                    // would serialise
-                    for (int rep = 0; rep < 2; ++rep) {
-                        const uint64_t act = __ballot(in);
-                        if (!act) break;
-                        const int leader = __ffsll((unsigned long long)act) - 1;
-                        const uint32_t dl = (uint32_t)__shfl((int)dig, leader, kWave);
-                        const bool mine = in && dig == dl;
-                        const uint64_t m = __ballot(mine);
-                        const uint64_t mass = wave_total_u64(mine ? (uint64_t)c : 0ull);
-                        if (lane == leader) {
-                            atomicAdd(&s_n[dl], (uint32_t)__popcll(m));
-                            atomicAdd(&s_mass[dl], (unsigned long long)mass);
-                        }
-                        in = in && !mine;
-                    }
-                    if (in) {
-                        atomicAdd(&s_n[dig], 1u);
-                        atomicAdd(&s_mass[dig], (unsigned long long)c);
-                    }
+        uint64_t all;
+        const uint64_t before = st.aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
+        if ((double)before < T && (double)(before + m) >= T) {
+            unsigned long long acc = before;
+            for (int q = 0; q < PER; ++q) {
+                const int64_t v = top - q;
+                if (v < (int64_t)st.lo) break;
+                const unsigned long long mv = (unsigned long long)v * ld_agent_u32(&a.h2[v - st.lo]);
+                if (mv == 0) continue;
+                if ((double)(acc + mv) >= T) {
+                    s_cs = (uint32_t)v;
+                    s_above = acc;
+                    break;
                 }
+                acc += mv;
             }
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                unsigned long long above = s_above;
-                uint32_t sel = 0;
-                for (int k = (1 << bits) - 1; k >= 0; --k) {
-                    if (s_n[k] == 0) continue;
-                    if ((double)(above + s_mass[k]) >= T) { sel = (uint32_t)k; break; }
-                    above += s_mass[k];
+        }
+        __syncthreads();
+    } else {
+        // the bucket's counts, sorted: c* is the largest count whose mass
+        // from the top reaches T
+        const int32_t L = min((int32_t)ld_agent_u32(&a.state->list_n), kTrimList);
+        const int P = pow2_at_least(L > 1 ? L : 2);
+        for (int q = threadIdx.x; q < P; q += NT) s_l[q] = q < L ? (uint64_t)a.list[q] : 0ull;
+        bitonic_sort_u64<NT>(s_l, P);                          // ascending; ends with a barrier
+        // the j-th largest is s_l[P - 1 - j]; thread i takes j in [PJ i, PJ (i + 1))
+        const int PJ = (P + NT - 1) / NT;
+        uint64_t m = 0;
+        for (int q = 0; q < PJ; ++q) {
+            const int j = PJ * (int)threadIdx.x + q;
+            if (j < P) m += s_l[P - 1 - j];
+        }
+        uint64_t all;
+        const uint64_t before = st.aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
+        if ((double)before < T && (double)(before + m) >= T) {
+            unsigned long long acc = before;
+            for (int q = 0; q < PJ; ++q) {
+                const int j = PJ * (int)threadIdx.x + q;
+                if (j >= P) break;
+                const uint64_t v = s_l[P - 1 - j];
+                if ((double)(acc + v) >= T) {
+                    s_cs = (uint32_t)v;
+                    break;
                 }
-                s_prefix = pre | (sel << shift);
-                s_above = above;
+                acc += v;
             }
-            __syncthreads();
         }
-        if (threadIdx.x == 0) {
-            // the fewest ids of count c* that bring the mass to T (the mass
-            // above c* is below T, and all of c*'s ids reach it)
-            const uint32_t cs = s_prefix;
-            const unsigned long long above = s_above;
-            const double need = ceil((T - (double)above) / (double)cs);
-            uint32_t take = need < 1.0 ? 1u : (uint32_t)need;
-            while (take > 1 && (double)(above + (unsigned long long)(take - 1) * cs) >= T) --take;
-            while ((double)(above + (unsigned long long)take * cs) < T) ++take;
-            s_cstar = cs;
-            s_take = take;
-        }
+        __syncthreads();
+        // the mass strictly above c* (entries equal to c* may come before the crossing)
+        const uint32_t cs = s_cs;
+        uint64_t mg = 0;
+        for (int q = threadIdx.x; q < P; q += NT)
+            if (s_l[q] > cs) mg += s_l[q];
+        uint64_t g;
+        (void)wg_excl_scan_u64<NT>(mg, s_tmp, &g);
+        if (threadIdx.x == 0) s_above = st.aboveB + g;
         __syncthreads();
     }
-    const uint32_t cstar = s_cstar;
-    const int32_t take = (int32_t)s_take;
-    // rank of each flagged id in id order: U sub-rounds of NT ids per round
-    int32_t run = 0;          // flagged ids in earlier rounds (same in every thread)
-    auto rank_round = [&](const bool (&f)[U], int32_t (&rank)[U]) -> int32_t {
-        uint64_t bal[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            bal[u] = __ballot(f[u]);
-            if (lane == 0) s_cnt[u][wv] = (int32_t)__popcll(bal[u]);
-        }
-        __syncthreads();
-        int32_t base = run, total = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int32_t sub = 0, below = 0;
-            for (int w = 0; w < NW; ++w) {
-                const int32_t n = s_cnt[u][w];
-                if (w < wv) below += n;
-                sub += n;
-            }
-            rank[u] = base + below + (int32_t)__popcll(bal[u] & ((1ull << lane) - 1ull));
-            base += sub;
-            total += sub;
-        }
-        __syncthreads();
-        return total;
-    };
-    if (mode == 2) {
-        // the take-th lowest id of count c*
-        for (int32_t tb = 0; tb < Vt; tb += U * NT) {
-            uint32_t cc[U];
-            load_round(tb, cc);
-            bool f[U];
-            int32_t rk[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) f[u] = cc[u] == cstar;
-            const int32_t tot = rank_round(f, rk);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (f[u] && rk[u] == take - 1) s_tie = tb + u * NT + (int32_t)threadIdx.x;
-            run += tot;
-            if (run >= take) break;                          // uniform: every thread holds run
-        }
-        __syncthreads();
-        run = 0;
-    }
-    const int32_t tie = s_tie;
-    auto kept = [&](uint32_t c, int32_t t) -> bool {
-        if (mode == 0 || c == 0) return false;
-        if (mode == 1) return true;
-        return c > cstar || (c == cstar && t <= tie);
-    };
-    unsigned long long mass = 0;
-    for (int32_t tb = 0; tb < Vt; tb += U * NT) {
-        uint32_t cc[U];
-        load_round(tb, cc);
-        bool f[U];
-        int32_t rk[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t t = tb + u * NT + (int32_t)threadIdx.x;
-            f[u] = t < Vt && kept(cc[u], t);
-            if (f[u]) mass += cc[u];
-        }
-        const int32_t tot = rank_round(f, rk);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int32_t t = tb + u * NT + (int32_t)threadIdx.x;
-            if (f[u]) a.out_d2t[rk[u]] = t;
-            if (a.out_t2d && t < Vt) a.out_t2d[t] = f[u] ? rk[u] : -1;
-        }
-        run += tot;
-    }
-    mass = wave_total_u64(mass);
-    if (lane == 0) s_mtot[wv] = mass;
-    __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned long long m = 0;
-        for (int w = 0; w < NW; ++w) m += s_mtot[w];
-        *a.out_vd = run;
+        TrimState o = st;
+        const uint32_t cs = s_cs > 0 ? s_cs : st.lo;          // found by construction
+        o.cstar = cs;
+        o.above = s_above;
+        o.take = trim_take(T, o.above, cs);
+        *a.state = o;
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void trim_refine_kernel(TrimArgs a) {
+    __shared__ int s_last;
+    const TrimState st = *a.state;
+    if (st.mode != 2 || st.refine == 0) return;               // alike in every workgroup: none arrives
+    const int32_t t0 = ((int32_t)blockIdx.x * NT + (int32_t)threadIdx.x) * 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int32_t t = t0 + u;
+        const uint32_t c = t < a.Vt ? a.counts[t] : 0u;
+        const bool in = c >= st.lo && c <= st.hi && c > 0;
+        if (st.refine == 1) {
+            wave_aggregate<false>(in, (int)(c - st.lo), 0ull,
+                                  [&](int k, uint32_t n, uint64_t) { atomicAdd(&a.h2[k], n); });
+        } else {
+            const int32_t pos = wave_append(in, reinterpret_cast<int32_t *>(&a.state->list_n));
+            if (in && pos < kTrimList) a.list[pos] = c;
+        }
+    }
+    if (!arrive_last(&a.arrive[1], gridDim.x, &s_last)) return;
+    trim_cut<NT>(a, st);
+}
+
+// ---------------------------------------------------------------------------
+// Launches 4 and 5: block counts, then d2t / t2d
+// ---------------------------------------------------------------------------
+struct TrimCut {
+    int mode;
+    uint32_t cstar;
+    __device__ __forceinline__ bool def(uint32_t c) const { return mode == 1 ? c > 0 : (mode == 2 && c > cstar); }
+    __device__ __forceinline__ bool tie(uint32_t c) const { return mode == 2 && c == cstar; }
+};
+
+template <int NT>
+__global__ __launch_bounds__(NT) void trim_count_kernel(TrimArgs a) {
+    static_assert(NT * 4 == kTrimBlock, "four ids per thread");
+    __shared__ uint64_t s_tmp[NT / kWave];
+    const TrimState st = *a.state;
+    const TrimCut cut{st.mode, st.cstar};
+    const int32_t t0 = (int32_t)blockIdx.x * kTrimBlock + (int32_t)threadIdx.x * 4;
+    uint32_t nd = 0, nt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int32_t t = t0 + u;
+        const uint32_t c = t < a.Vt ? a.counts[t] : 0u;
+        nd += cut.def(c) ? 1u : 0u;
+        nt += cut.tie(c) ? 1u : 0u;
+    }
+    uint64_t tot;
+    (void)wg_excl_scan_u64<NT>(((uint64_t)nd << 32) | nt, s_tmp, &tot);
+    if (threadIdx.x == 0) {
+        a.blockdef[blockIdx.x] = (uint32_t)(tot >> 32);
+        a.blocktie[blockIdx.x] = (uint32_t)tot;
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void trim_write_kernel(TrimArgs a) {
+    static_assert(NT * 4 == kTrimBlock, "four ids per thread");
+    __shared__ uint64_t s_tmp[NT / kWave];
+    const TrimState st = *a.state;
+    const TrimCut cut{st.mode, st.cstar};
+    const uint32_t take = st.mode == 2 ? st.take : 0u;
+    const int32_t j = blockIdx.x;
+    // ids above the cut and on it in the blocks before this one
+    uint64_t pre = 0;
+    for (int32_t q = threadIdx.x; q < j; q += NT) pre += ((uint64_t)a.blockdef[q] << 32) | a.blocktie[q];
+    uint64_t before;
+    (void)wg_excl_scan_u64<NT>(pre, s_tmp, &before);
+    const int32_t t0 = j * kTrimBlock + (int32_t)threadIdx.x * 4;
+    uint32_t c[4], nd = 0, nt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int32_t t = t0 + u;
+        c[u] = t < a.Vt ? a.counts[t] : 0u;
+        nd += cut.def(c[u]) ? 1u : 0u;
+        nt += cut.tie(c[u]) ? 1u : 0u;
+    }
+    uint64_t blk;
+    const uint64_t ex = wg_excl_scan_u64<NT>(((uint64_t)nd << 32) | nt, s_tmp, &blk);
+    uint32_t rd = (uint32_t)(before >> 32) + (uint32_t)(ex >> 32);     // ids above the cut before t
+    uint32_t rt = (uint32_t)before + (uint32_t)ex;                     // ids on the cut before t
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int32_t t = t0 + u;
+        if (t >= a.Vt) break;
+        const bool d = cut.def(c[u]), e = cut.tie(c[u]);
+        const bool kept = d || (e && rt < take);
+        const uint32_t pos = rd + (rt < take ? rt : take);
+        if (kept) a.out_d2t[pos] = t;
+        if (a.out_t2d) a.out_t2d[t] = kept ? (int32_t)pos : -1;
+        rd += d ? 1u : 0u;
+        rt += e ? 1u : 0u;
+    }
+    if (j == a.nblocks - 1 && threadIdx.x == 0) {
+        const uint32_t nd_all = (uint32_t)(before >> 32) + (uint32_t)(blk >> 32);
+        const uint32_t nt_all = (uint32_t)before + (uint32_t)blk;
+        *a.out_vd = (int32_t)(nd_all + (nt_all < take ? nt_all : take));
         if (a.out_info) {
-            a.out_info[0] = (int64_t)m;
-            a.out_info[1] = (int64_t)valid;
-            a.out_info[2] = (int64_t)invalid;
+            const unsigned long long mass =
+                st.mode == 2 ? st.above + (unsigned long long)take * st.cstar : (st.mode == 1 ? st.valid : 0ull);
+            a.out_info[0] = (int64_t)mass;
+            a.out_info[1] = (int64_t)st.valid;
+            a.out_info[2] = (int64_t)st.invalid;
         }
-        a.totals[0] = 0;
-        a.totals[1] = 0;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int32_t trim_ranges(int32_t Vt) { return (Vt + kTrimBins - 1) / kTrimBins; }
-int32_t trim_slices(int32_t Vt) {
-    int32_t s = kTrimTargetWgs / trim_ranges(Vt);
+namespace {
+struct TrimGeom {
+    int32_t R, logR, KB, S, nblocks;
+};
+TrimGeom trim_geom(int32_t Vt) {
+    TrimGeom g;
+    g.logR = 0;
+    while ((((int64_t)Vt + ((int64_t)1 << g.logR) - 1) >> g.logR) > kTrimBins) ++g.logR;
+    g.R = 1 << g.logR;
+    g.KB = (int32_t)(((((int64_t)Vt + g.R - 1) >> g.logR) + 3) & ~(int64_t)3);    // bins per range, padded to 4
+    int32_t s = kTrimTargetWgs / g.R;
     if (s < 1) s = 1;
     if (s > kTrimMaxSlices) s = kTrimMaxSlices;
-    return s;
+    g.S = s;
+    g.nblocks = (Vt + kTrimBlock - 1) / kTrimBlock;
+    return g;
 }
+struct TrimSizes {
+    size_t part, counts, hn, hm, h2, list, bd, st, total;
+};
+TrimSizes trim_sizes(int32_t Vt) {
+    const TrimGeom g = trim_geom(Vt);
+    TrimSizes z;
+    // S R <= max(kTrimTargetWgs, R) and KB <= min(kTrimBins, Vt): a bound
+    // that never shrinks as Vt grows, so a workspace sized for one vocabulary
+    // serves every smaller one
+    const size_t sr = (size_t)(g.R > kTrimTargetWgs ? g.R : kTrimTargetWgs);
+    const size_t kb = (size_t)(Vt < kTrimBins ? (Vt + 3) & ~3 : kTrimBins);
+    z.part = align256(sizeof(uint32_t) * sr * kb);
+    z.counts = align256(sizeof(uint32_t) * (size_t)Vt);
+    z.hn = align256(sizeof(uint32_t) * kTrimBuckets);
+    z.hm = align256(sizeof(unsigned long long) * kTrimBuckets);
+    z.h2 = align256(sizeof(uint32_t) * kTrimFine);
+    z.list = align256(sizeof(uint32_t) * kTrimList);
+    z.bd = align256(sizeof(uint32_t) * (size_t)g.nblocks);
+    z.st = align256(sizeof(TrimState));
+    z.total = z.part + z.counts + z.hn + z.hm + z.h2 + z.list + 2 * z.bd + z.st;
+    return z;
+}
+}  // namespace
+
 size_t trim_counter_bytes(int32_t Vt) { (void)Vt; return 256; }
-size_t trim_data_bytes(int32_t Vt) {
-    return align256(sizeof(uint32_t) * (size_t)trim_slices(Vt) * Vt) + align256(sizeof(uint32_t) * (size_t)Vt);
+size_t trim_data_bytes(int32_t Vt) { return trim_sizes(Vt).total; }
+
+void trim_layout(TrimArgs &a, char *base, char *data) {
+    const TrimGeom g = trim_geom(a.Vt);
+    const TrimSizes z = trim_sizes(a.Vt);
+    a.R = g.R;
+    a.logR = g.logR;
+    a.KB = g.KB;
+    a.S = g.S;
+    a.nblocks = g.nblocks;
+    a.totals = reinterpret_cast<unsigned long long *>(base);
+    a.arrive = reinterpret_cast<uint32_t *>(base + 2 * sizeof(unsigned long long));
+    char *p = data;
+    a.part = reinterpret_cast<uint32_t *>(p);
+    p += z.part;
+    a.counts = reinterpret_cast<uint32_t *>(p);
+    p += z.counts;
+    a.hist_n = reinterpret_cast<uint32_t *>(p);
+    p += z.hn;
+    a.hist_m = reinterpret_cast<unsigned long long *>(p);
+    p += z.hm;
+    a.h2 = reinterpret_cast<uint32_t *>(p);
+    p += z.h2;
+    a.list = reinterpret_cast<uint32_t *>(p);
+    p += z.list;
+    a.blockdef = reinterpret_cast<uint32_t *>(p);
+    p += z.bd;
+    a.blocktie = reinterpret_cast<uint32_t *>(p);
+    p += z.bd;
+    a.state = reinterpret_cast<TrimState *>(p);
 }
 
 hipError_t launch_trim(const TrimArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((trim_part_kernel<kTrimPartThreads, kTrimPartUnroll>),
-                       dim3((unsigned)(trim_ranges(a.Vt) * a.S)), dim3(kTrimPartThreads), 0, st, a);
+    hipLaunchKernelGGL((trim_part_kernel<kTrimPartThreads, kTrimPartUnroll>), dim3((unsigned)(a.R * a.S)),
+                       dim3(kTrimPartThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((trim_reduce_kernel<256>), dim3((unsigned)((a.Vt + 255) / 256)), dim3(256), 0, st, a);
+    const int64_t nred = ((int64_t)a.R * (a.KB / 4) + kTrimThreads - 1) / kTrimThreads;
+    hipLaunchKernelGGL((trim_reduce_kernel<kTrimThreads>), dim3((unsigned)nred), dim3(kTrimThreads), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((trim_select_kernel<kTrimSelThreads, kTrimSelUnroll>), dim3(1), dim3(kTrimSelThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((trim_refine_kernel<kTrimThreads>), dim3((unsigned)a.nblocks), dim3(kTrimThreads), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((trim_count_kernel<kTrimThreads>), dim3((unsigned)a.nblocks), dim3(kTrimThreads), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((trim_write_kernel<kTrimThreads>), dim3((unsigned)a.nblocks), dim3(kTrimThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -92,3 +92,39 @@ def test_trim_map_feeds_verification(oracle_mod):
     out = run_sample(ws)
     assert not (out["status"] & 2).any()
     compare_sample(ws, out, oracle_mod)
+
+
+def _stream_from_counts(rng, counts):
+    """A shuffled stream in which id t occurs counts[t] times."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return rng.permutation(ids)
+
+
+@pytest.mark.parametrize("P", [0.5, 0.9, 0.123])
+def test_trim_cut_in_a_wide_bucket(oracle_mod, P):
+    """Counts of 128..1200 put the cut in a count bucket several counts wide,
+    with many ids on each count: the exact histogram inside the bucket."""
+    rng = np.random.default_rng(9410)
+    counts = rng.integers(128, 1200, size=2000)
+    o = _check(oracle_mod, _stream_from_counts(rng, counts), 2000, P)
+    _say("wide bucket P=%g: kept %d ids" % (P, len(o[0])))
+
+
+@pytest.mark.parametrize("P", [0.5, 0.62, 0.3, 0.99])
+def test_trim_cut_among_huge_counts(oracle_mod, P):
+    """A few ids with counts above 2^19 hold the cut: buckets that wide are
+    refined from a sorted list of their counts (ties included)."""
+    rng = np.random.default_rng(9411)
+    counts = np.full(300, 5, np.int64)
+    counts[[3, 17, 40, 41, 99, 250]] = [600000, 590000, 580000, 570001, 570001, 560000]
+    o = _check(oracle_mod, _stream_from_counts(rng, counts), 300, P)
+    _say("huge counts P=%g: kept %d ids" % (P, len(o[0])))
+
+
+def test_trim_large_vocab_and_one_id(oracle_mod):
+    """A vocabulary of 2^20 ids (64 residue ranges, 4 slices) and one of a
+    single id."""
+    w = synth.token_stream(9412, N=1 << 20, Vt=1 << 20, s=1.05, invalid_frac=0.001)
+    _check(oracle_mod, w["tokens"], 1 << 20, 0.95)
+    _check(oracle_mod, np.zeros(1000, np.int32), 1, 0.95)
+    _check(oracle_mod, np.array([0, 3, 3, -7], np.int32), 1, 0.5)
