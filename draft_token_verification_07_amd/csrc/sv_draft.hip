@@ -374,15 +374,23 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
             if (threadIdx.x == 0) s_cnt2 = 0;
             __syncthreads();
             if (C > 1) {
-                for (int32_t k = 0; k < C; ++k) {
-                    const int32_t nk = s_res[k].n;
-                    const uint64_t *src = a.cand + ((size_t)b * C + k) * kCandCap;
-                    for (int32_t e0 = 0; e0 < nk; e0 += NT) {
-                        const int32_t e = e0 + (int32_t)threadIdx.x;
-                        const uint64_t P = e < nk ? sub_u64(&src[e]) : 0ull;
-                        const bool in = e < nk && fkey_inv(pkey(P)) >= thr;
+                // one load per chunk in flight before any is used (the usual
+                // band fits one round); the order of the codes is free
+                int32_t nmax = 0;
+                for (int32_t k = 0; k < C; ++k) nmax = max(nmax, s_res[k].n);
+                const uint64_t *src = a.cand + (size_t)b * C * kCandCap;
+                for (int32_t e0 = 0; e0 < nmax; e0 += NT) {
+                    const int32_t e = e0 + (int32_t)threadIdx.x;
+                    uint64_t Pk[kDraftMaxChunks];
+#pragma unroll
+                    for (int32_t k = 0; k < kDraftMaxChunks; ++k)
+                        Pk[k] = (k < C && e < s_res[k].n) ? sub_u64(&src[(size_t)k * kCandCap + e]) : 0ull;
+#pragma unroll
+                    for (int32_t k = 0; k < kDraftMaxChunks; ++k) {
+                        if (k >= C) break;                       // alike in every thread
+                        const bool in = e < s_res[k].n && fkey_inv(pkey(Pk[k])) >= thr;
                         const int32_t pos = wave_append(in, &s_cnt2);
-                        if (in && pos < kCandCap) s_cum[pos] = P;
+                        if (in && pos < kCandCap) s_cum[pos] = Pk[k];
                     }
                 }
                 __syncthreads();
@@ -397,7 +405,79 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
         }
         int32_t K = 0, P2 = 2;
         uint64_t Zkf = 0;
-        if (!fallback) {
+        bool fast_done = false;
+        if (!fallback && topk_on && a.top_k <= kWave) {
+            // ---- top_k <= 64: only the first 64 positions of the stable order
+            // can be kept.  Each wave keeps the 64 largest ordering codes of
+            // its share by in-wave bitonic networks (no workgroup barrier),
+            // wave 0 merges the waves' lists and takes the weights, the top-p
+            // count and the draw in registers: the arithmetic of the sorted
+            // path below, on its first 64 positions.
+            __shared__ uint64_t s_top[NW * kWave];
+            __shared__ unsigned long long s_zk;
+            __shared__ int s_fb;
+            uint64_t top = 0;                                    // codes are > 0: 0 is empty
+            for (int32_t e0 = wv * kWave; e0 < nc; e0 += NT) {
+                const int32_t e = e0 + lane;
+                top = wave_merge_top_u64(top, wave_sort_desc_u64(e < nc ? s_P[e] : 0ull));
+            }
+            // the waves' lists merge as a tree: wave w takes wave w + h's
+            // list, h = NW / 2, NW / 4, ..., 1
+            s_top[wv * kWave + lane] = top;
+            __syncthreads();
+#pragma unroll
+            for (int h = NW / 2; h > 1; h >>= 1) {
+                if (wv < h) {
+                    top = wave_merge_top_u64(top, s_top[(wv + h) * kWave + lane]);
+                    s_top[wv * kWave + lane] = top;
+                }
+                __syncthreads();
+            }
+            if (wv == 0) {
+                const uint64_t t = wave_merge_top_u64(top, s_top[kWave + lane]);
+                const int32_t nv = min(nc, (int32_t)kWave);
+                const bool has = lane < nv;
+                const uint32_t fw = has ? fixw32(fkey_inv(pkey(t)), m, c) : 0u;
+                const uint64_t cum = wave_incl_scan_u64_dpp((uint64_t)fw);
+                int32_t kp = INT32_MAX;                          // no top-p cut in the first 64
+                bool fb = false;
+                if (topp_on) {
+                    const double T0 = (double)a.top_p * (double)Z;
+                    if (!(T0 < kFixSelMaxMass)) {
+                        fb = true;
+                    } else {
+                        const uint64_t over = __ballot(has && cum > (uint64_t)(T0 * kFixW));
+                        if (over) kp = __ffsll((unsigned long long)over);
+                    }
+                }
+                const int32_t Kf = min(a.top_k, kp);
+                fb = fb || Kf > nv;
+                if (!fb) {
+                    const uint64_t zk = readlane_u64(cum, Kf - 1);
+                    const uint64_t target = frac_floor(u, zk);
+                    // entry q sums the kept weights of ids <= its own
+                    const int32_t id = lane < Kf ? pid(t) : INT32_MAX;
+                    uint64_t incl = 0;
+                    for (int32_t j = 0; j < Kf; ++j) {
+                        const int32_t idj = __builtin_amdgcn_readlane(id, j);
+                        const uint32_t wj = (uint32_t)__builtin_amdgcn_readlane((int)fw, j);
+                        if (idj <= id) incl += wj;
+                    }
+                    const uint64_t hit = __ballot(lane < Kf && fw > 0 && incl > target && incl - fw <= target);
+                    const int32_t tk = hit ? __builtin_amdgcn_readlane(id, __ffsll((unsigned long long)hit) - 1) : -1;
+                    if (lane == 0) {
+                        s_tok = tk;
+                        s_zk = zk;
+                    }
+                }
+                if (lane == 0) s_fb = fb ? 1 : 0;
+            }
+            __syncthreads();
+            fallback = s_fb != 0;
+            fast_done = !fallback;
+            if (fast_done) Zkf = s_zk;
+        }
+        if (!fallback && !fast_done) {
             // descending order of the ordering codes: an ascending sort with
             // zero padding, read from the top (position s is s_P[P2 - 1 - s])
             P2 = pow2_at_least(nc < 2 ? 2 : nc);
@@ -440,7 +520,10 @@ __global__ __launch_bounds__(NT) void draft_kernel(DraftArgs a) {
             else if (!fallback) Zkf = s_cum[K - 1];
             __syncthreads();
         }
-        if (!fallback) {
+        if (fast_done) {
+            tok = s_tok;
+            if (tok >= 0) prob = exp2_hw((E::load(row, tok) - m) * c) / (float)((double)Zkf / kFixW);
+        } else if (!fallback) {
             // ---- the list draw: exact inverse CDF in id order over the first K
             const uint64_t target = frac_floor(u, Zkf);           // < Zkf
             if (threadIdx.x == 0) s_tok = -1;

@@ -617,6 +617,104 @@ __device__ __forceinline__ MaxSum wave_maxsum_dpp(MaxSum a, float c) {
     return r;
 }
 
+// 64-bit values across the lanes of a wave.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Lane l takes the value of lane l ^ J, by VALU cross-lane operations (no
+// LDS round trip): DPP quad permutes for 1 and 2, two DPP row permutes for 4
+// (row half mirror, then quad reverse) and 8 (row mirror, then row half
+// mirror), and the permlane swaps for 16 and 32 (with both operands x, lane l
+// of an even row or half gets x[l ^ J] in the second result, of an odd one
+// in the first).  Every lane of the wave takes part.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+    if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);
+    if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);
+    if constexpr (J == 4) {
+        const int t = __builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xf, 0xf, false);
+    }
+    if constexpr (J == 8) {
+        const int t = __builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, t, 0x141, 0xf, 0xf, false);
+    }
+    if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (threadIdx.x & 16) ? r[0] : r[1];
+    }
+    if constexpr (J == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+    return v;
+}
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v) {
+    return ((uint64_t)lane_xor_u32<J>((uint32_t)(v >> 32)) << 32) | lane_xor_u32<J>((uint32_t)v);
+}
+// Lane l takes lane 63 - l: row mirror (l ^ 15), then l ^ 16 and l ^ 32.
+__device__ __forceinline__ uint64_t lane_reverse_u64(uint64_t v) {
+    auto rev = [](uint32_t x) {
+        const uint32_t m = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xf, 0xf, false);
+        return lane_xor_u32<32>(lane_xor_u32<16>(m));
+    };
+    return ((uint64_t)rev((uint32_t)(v >> 32)) << 32) | rev((uint32_t)v);
+}
+
+// One compare-exchange stage of a bitonic network over the wave: partner
+// l ^ J; the lower lane of the pair keeps the larger when `desc`.
+template <int J>
+__device__ __forceinline__ uint64_t wave_cx_u64(uint64_t v, bool desc) {
+    const uint64_t o = lane_xor_u64<J>(v);
+    const bool low = (threadIdx.x & J) == 0;
+    return (low == desc) ? (v > o ? v : o) : (v < o ? v : o);
+}
+// Bitonic sort of one value per lane, descending across the wave (lane 0
+// the largest); every lane takes part.  Runs of length k alternate direction
+// until the last (k = 64), which is descending.
+__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+    v = wave_cx_u64<1>(v, (lane & 2) == 0);
+    v = wave_cx_u64<2>(v, (lane & 4) == 0);
+    v = wave_cx_u64<1>(v, (lane & 4) == 0);
+    v = wave_cx_u64<4>(v, (lane & 8) == 0);
+    v = wave_cx_u64<2>(v, (lane & 8) == 0);
+    v = wave_cx_u64<1>(v, (lane & 8) == 0);
+    v = wave_cx_u64<8>(v, (lane & 16) == 0);
+    v = wave_cx_u64<4>(v, (lane & 16) == 0);
+    v = wave_cx_u64<2>(v, (lane & 16) == 0);
+    v = wave_cx_u64<1>(v, (lane & 16) == 0);
+    v = wave_cx_u64<16>(v, (lane & 32) == 0);
+    v = wave_cx_u64<8>(v, (lane & 32) == 0);
+    v = wave_cx_u64<4>(v, (lane & 32) == 0);
+    v = wave_cx_u64<2>(v, (lane & 32) == 0);
+    v = wave_cx_u64<1>(v, (lane & 32) == 0);
+    v = wave_cx_u64<32>(v, true);
+    v = wave_cx_u64<16>(v, true);
+    v = wave_cx_u64<8>(v, true);
+    v = wave_cx_u64<4>(v, true);
+    v = wave_cx_u64<2>(v, true);
+    v = wave_cx_u64<1>(v, true);
+    return v;
+}
+// The kWave largest of two descending wave lists, descending: the larger of
+// a[l] and b[63 - l] in each lane forms a bitonic sequence holding them,
+// which a half cleaner network sorts.
+__device__ __forceinline__ uint64_t wave_merge_top_u64(uint64_t a, uint64_t b) {
+    const uint64_t br = lane_reverse_u64(b);
+    uint64_t v = a > br ? a : br;
+    v = wave_cx_u64<32>(v, true);
+    v = wave_cx_u64<16>(v, true);
+    v = wave_cx_u64<8>(v, true);
+    v = wave_cx_u64<4>(v, true);
+    v = wave_cx_u64<2>(v, true);
+    v = wave_cx_u64<1>(v, true);
+    return v;
+}
+
 // Inclusive prefix sum of a u64 across a wave (lane order).
 __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
     const int lane = threadIdx.x & (kWave - 1);

@@ -172,11 +172,6 @@ __device__ SV_RARE void band_radix(const uint64_t *s_P, const uint32_t *s_fw, un
 // copied to LDS), then expand the band, select the kept set, and publish the
 // row descriptor and kept list.  s_lds is 32 KiB: band tokens in its first
 // half, band vectors in its second.
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
 // Top-p select over the band by bins (the usual case).  The band tokens are
 // binned by their distance below the row maximum: kWave bins of equal width,
 // so a lower bin holds only larger logits and equal logits share a bin.  Per-bin
