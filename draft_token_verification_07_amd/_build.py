@@ -16,8 +16,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["sv_api.hip", "sv_greedy.hip", "sv_sample.hip", "sv_draft.hip", "sv_fanout.hip", "sv_trim.hip", "sv_lmhead.hip"]
-HEADERS = ["sv_common.h", "sv_internal.h", "sv_rows.h"]
+SOURCES = ["sv_host.cpp", "sv_api.hip", "sv_greedy.hip", "sv_sample.hip", "sv_draft.hip", "sv_fanout.hip", "sv_trim.hip", "sv_lmhead.hip"]
+HEADERS = ["sv_host.h", "sv_common.h", "sv_internal.h", "sv_rows.h"]
 
 
 def hipcc() -> str:

@@ -1,7 +1,8 @@
-// sv_api.hip -- the C ABI of libspecverify: argument checks, workspace
-// sizing and launch dispatch.  No allocation, no synchronization: every
-// launch goes to the caller's stream, and host-detectable argument errors
-// return before anything is launched.
+// sv_api.hip -- the launching entry points of the C ABI of libspecverify:
+// each runs its argument check (sv_host.cpp), fills the argument block and
+// dispatches the launches.  No allocation, no synchronization: every launch
+// goes to the caller's stream, and host-detectable argument errors return
+// before anything is launched.
 #include <math.h>
 #include <stdint.h>
 
@@ -56,28 +57,6 @@ sv_status scratch_for_current_device(hipStream_t stream, void **out) {
 
 namespace {
 
-bool dtype_ok(int dt) { return dt == SV_F32 || dt == SV_BF16; }
-size_t esize(int dt) { return dt == SV_BF16 ? 2 : 4; }
-bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// The whole grid must fit one launch dimension.
-bool grid_fits(int64_t wgs) { return wgs >= 0 && wgs <= (int64_t)INT32_MAX; }
-
-// greedy / tree: counters [B] (+ [B, R] when rows are chunked) below K;
-// (value, index) row results [B, R] and chunk partials [B, R, C] above
-int32_t greedy_C(int32_t B, int32_t R, int32_t V) { return greedy_chunks(V, (int64_t)B * R); }
-size_t greedy_counter_bytes(int32_t B, int32_t R, int32_t V) {
-    const int32_t C = greedy_C(B, R, V);
-    return align256(sizeof(uint32_t) * (size_t)B * (C > 1 && !greedy_split(R, C) ? 1 + (size_t)R : 1));
-}
-size_t greedy_rowres_bytes(int32_t B, int32_t R) { return align256(sizeof(ArgMax) * (size_t)B * R); }
-size_t greedy_data_bytes(int32_t B, int32_t R, int32_t V) {
-    return greedy_rowres_bytes(B, R) + align256(sizeof(ArgMax) * (size_t)B * R * greedy_C(B, R, V));
-}
-size_t greedy_ws(int32_t B, int32_t R, int32_t V) {
-    return workspace_need(greedy_counter_bytes(B, R, V), greedy_data_bytes(B, R, V));
-}
-
 sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, const int32_t *parents,
                      int32_t B, int32_t R, int32_t V, bool tree, int32_t *out_tokens, int32_t *out_len,
                      int32_t *out_status, int32_t *out_path, void *ws, size_t ws_bytes, hipStream_t st) {
@@ -95,64 +74,67 @@ sv_status run_greedy(const void *logits, sv_dtype dt, const int32_t *tokens, con
     a.out_len = out_len;
     a.out_status = out_status;
     a.out_path = out_path;
-    if (!workspace_fits(ws_bytes, greedy_counter_bytes(B, R, V), greedy_data_bytes(B, R, V)))
-        return SV_ERR_WORKSPACE_TOO_SMALL;
     char *base = static_cast<char *>(ws);
     char *data = base + counter_region(ws_bytes);
     a.counters = reinterpret_cast<uint32_t *>(base);
     a.rowres = reinterpret_cast<ArgMax *>(data);
     a.part = reinterpret_cast<ArgMax *>(data + greedy_rowres_bytes(B, R));
-    if (!grid_fits((int64_t)B * R * a.chunks)) return SV_ERR_TOO_LARGE;
     return launch_greedy(a, dt, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status run_lmhead(const void *hidden, const void *W, const int32_t *tokens, const int32_t *parents, int32_t B,
+                     int32_t R, int32_t d, int32_t V, bool tree, int32_t *out_path, int32_t *out_tokens,
+                     int32_t *out_len, int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *ws,
+                     size_t ws_bytes, hipStream_t st) {
+    const int64_t M = (int64_t)B * R;
+    const size_t nt = ((size_t)V + kLmTile - 1) / kLmTile;
+    LmheadArgs L;
+    L.hidden = static_cast<const uint16_t *>(hidden);
+    L.W = static_cast<const uint16_t *>(W);
+    L.M = (int32_t)M;
+    L.d = d;
+    L.V = V;
+    L.mtiles = (int32_t)((M + kLmTile - 1) / kLmTile);
+    L.ntiles = (int32_t)nt;
+    L.ntiles8 = (int32_t)(((nt + 1) / 2 + 7) / 8 * 8);
+    char *data = static_cast<char *>(ws) + counter_region(ws_bytes);
+    L.part = reinterpret_cast<uint64_t *>(data);
+    L.rowres = reinterpret_cast<ArgMax *>(data + lmhead_part_bytes(M, V));
+    L.out_argmax = out_argmax;
+    L.out_maxlogit = out_maxlogit;
+    if (launch_lmhead(L, st) != hipSuccess) return SV_ERR_HIP;
+    GreedyArgs a;
+    a.logits = nullptr;
+    a.tokens = tokens;
+    a.parents = parents;
+    a.B = B;
+    a.rows_per_seq = R;
+    a.V = V;
+    a.chunks = 1;
+    a.tree = tree ? 1 : 0;
+    a.split_chunks = 0;
+    a.out_tokens = out_tokens;
+    a.out_len = out_len;
+    a.out_status = out_status;
+    a.out_path = out_path;
+    a.part = nullptr;
+    a.rowres = L.rowres;
+    a.counters = nullptr;
+    return launch_seq(a, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // namespace
 
 extern "C" {
 
-const char *spec_verify_strerror(sv_status s) {
-    switch (s) {
-        case SV_OK: return "ok";
-        case SV_ERR_INVALID_ARG: return "invalid argument";
-        case SV_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
-        case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-        case SV_ERR_HIP: return "HIP launch error";
-        case SV_ERR_TOO_LARGE: return "size beyond library limits";
-    }
-    return "unknown status";
-}
-
-size_t sv_workspace_bytes_greedy(int32_t B, int32_t gamma, int32_t V) {
-    if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB) return 0;
-    return greedy_ws(B, gamma + 1, V);
-}
-
-size_t sv_workspace_bytes_tree(int32_t B, int32_t N, int32_t V) {
-    if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB) return 0;
-    return greedy_ws(B, N, V);
-}
-
-size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, float top_p) {
-    if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || Vt < 1 || Vd < 1 || Vt > SV_MAX_VOCAB ||
-        Vd > SV_MAX_VOCAB || !(top_p > 0.0f))
-        return 0;
-    WorkspaceLayout L;
-    int32_t ct, cd, tl, nt;
-    sample_layout(B, gamma, Vt, Vd, 4, 4, top_p < 1.0f, &L, &ct, &cd, &tl, &nt);
-    return workspace_need(L.counter_bytes, L.data_bytes);
-}
-
 sv_status spec_verify_greedy(const void *target_logits, sv_dtype dtype, const int32_t *draft_tokens,
                              int32_t B, int32_t gamma, int32_t V, int32_t *out_tokens,
                              int32_t *out_accept_len, int32_t *out_status, void *workspace,
                              size_t workspace_bytes, hipStream_t stream) {
-    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
-    if (B < 0 || gamma < 0 || V < 1) return SV_ERR_INVALID_ARG;
-    if (gamma > SV_MAX_GAMMA || V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!target_logits || !out_tokens || !out_accept_len || !workspace) return SV_ERR_INVALID_ARG;
-    if (gamma > 0 && !draft_tokens) return SV_ERR_INVALID_ARG;
-    if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
+    bool go;
+    const sv_status c = check_greedy(target_logits, dtype, draft_tokens, B, gamma, V, out_tokens, out_accept_len,
+                                     workspace, workspace_bytes, &go);
+    if (!go) return c;
     return run_greedy(target_logits, dtype, draft_tokens, nullptr, B, gamma + 1, V, false, out_tokens,
                       out_accept_len, out_status, nullptr, workspace, workspace_bytes, stream);
 }
@@ -162,14 +144,10 @@ sv_status spec_verify_tree_greedy(const void *target_logits, sv_dtype dtype, con
                                   int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
                                   int32_t *out_status, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
-    if (B < 0 || N < 1 || V < 1) return SV_ERR_INVALID_ARG;
-    if (N > SV_MAX_TREE_NODES || V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!target_logits || !node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len ||
-        !workspace)
-        return SV_ERR_INVALID_ARG;
-    if (!aligned(target_logits, esize(dtype))) return SV_ERR_INVALID_ARG;
+    bool go;
+    const sv_status c = check_tree(target_logits, dtype, node_tokens, parents, B, N, V, out_path_nodes, out_tokens,
+                                   out_accept_len, workspace, workspace_bytes, &go);
+    if (!go) return c;
     return run_greedy(target_logits, dtype, node_tokens, parents, B, N, V, true, out_tokens, out_accept_len,
                       out_status, out_path_nodes, workspace, workspace_bytes, stream);
 }
@@ -180,29 +158,13 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
                              int32_t Vt, int32_t Vd, float temperature, float top_p, int32_t *out_tokens,
                              int32_t *out_accept_len, float *out_p_tok, float *out_q_tok, int32_t *out_status,
                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!dtype_ok(target_dtype) || !dtype_ok(draft_dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
-    if (B < 0 || gamma < 0 || Vt < 1 || Vd < 1) return SV_ERR_INVALID_ARG;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
-    if (!(top_p > 0.0f)) return SV_ERR_INVALID_ARG;          // also rejects NaN
-    if (!d2t && Vd != Vt) return SV_ERR_INVALID_ARG;
-    if (d2t && Vd > Vt) return SV_ERR_INVALID_ARG;            // an injective map needs Vd <= Vt
-    if (gamma > SV_MAX_GAMMA || Vt > SV_MAX_VOCAB || Vd > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!target_logits || !u_sample || !out_tokens || !out_accept_len || !workspace) return SV_ERR_INVALID_ARG;
-    if (gamma > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SV_ERR_INVALID_ARG;
-    if (!aligned(target_logits, esize(target_dtype))) return SV_ERR_INVALID_ARG;
-    if (gamma > 0 && !aligned(draft_logits, esize(draft_dtype))) return SV_ERR_INVALID_ARG;
-
-    const bool topp = top_p < 1.0f;
     WorkspaceLayout L;
-    int32_t Ct, Cd, tl, nt;
-    sample_layout(B, gamma, Vt, Vd, esize(target_dtype), esize(draft_dtype), topp, &L, &Ct, &Cd, &tl, &nt);
-    if (!workspace_fits(workspace_bytes, L.counter_bytes, L.data_bytes)) return SV_ERR_WORKSPACE_TOO_SMALL;
-    const int64_t NR = 2 * (int64_t)gamma + 1;
-    if (!grid_fits((int64_t)B * (topp ? NR : (1 + (int64_t)(gamma + 1) * Ct + (int64_t)gamma * Cd))) ||
-        !grid_fits((int64_t)B * nt))
-        return SV_ERR_TOO_LARGE;
-
+    int32_t Ct = 1, Cd = 1, tl = 1, nt = 1;
+    bool go;
+    const sv_status c = check_sample(target_logits, target_dtype, draft_logits, draft_dtype, draft_tokens, d2t,
+                                     u_accept, u_sample, B, gamma, Vt, Vd, temperature, top_p, out_tokens,
+                                     out_accept_len, workspace, workspace_bytes, &L, &Ct, &Cd, &tl, &nt, &go);
+    if (!go) return c;
     SampleArgs a;
     a.tl = target_logits;
     a.dl = draft_logits;
@@ -217,7 +179,7 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.T = temperature;
     a.c = 1.4426950408889634f / temperature;     // log2(e) / T: 2^((z - m) c) = e^((z - m) / T)
     a.top_p = top_p;
-    a.topp = topp ? 1 : 0;
+    a.topp = top_p < 1.0f ? 1 : 0;
     a.Ct = Ct;
     a.Cd = Cd;
     a.tile = tl;
@@ -240,35 +202,19 @@ sv_status spec_verify_sample(const void *target_logits, sv_dtype target_dtype, c
     a.tile_mass = reinterpret_cast<uint64_t *>(data + L.tile_mass);
     a.tile_sub = reinterpret_cast<uint64_t *>(data + L.tile_sub);
     a.tile_jb = reinterpret_cast<int32_t *>(data + L.tile_jb);
-
     return launch_sample(a, target_dtype, draft_dtype, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
-}
-
-size_t sv_workspace_bytes_draft(int32_t B, int32_t V) {
-    if (B < 0 || V < 1 || V > SV_MAX_VOCAB) return 0;
-    DraftLayout L;
-    int32_t C;
-    draft_layout(B, V, &L, &C);
-    return workspace_need(L.counter_bytes, L.data_bytes);
 }
 
 sv_status spec_draft_sample(const void *logits, sv_dtype dtype, const int32_t *d2t, const float *u, int32_t B,
                             int32_t V, float temperature, float top_p, int32_t top_k, int32_t *out_tokens,
                             float *out_prob, int32_t *out_status, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-    if (!dtype_ok(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
-    if (B < 0 || V < 1) return SV_ERR_INVALID_ARG;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
-    if (!(top_p > 0.0f)) return SV_ERR_INVALID_ARG;
-    if (V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!logits || !u || !out_tokens || !workspace) return SV_ERR_INVALID_ARG;
-    if (!aligned(logits, esize(dtype))) return SV_ERR_INVALID_ARG;
     DraftLayout L;
-    int32_t C;
-    draft_layout(B, V, &L, &C);
-    if (!workspace_fits(workspace_bytes, L.counter_bytes, L.data_bytes)) return SV_ERR_WORKSPACE_TOO_SMALL;
-    if (!grid_fits((int64_t)B * C)) return SV_ERR_TOO_LARGE;
+    int32_t C = 1;
+    bool go;
+    const sv_status c = check_draft(logits, dtype, u, B, V, temperature, top_p, out_tokens, workspace,
+                                    workspace_bytes, &L, &C, &go);
+    if (!go) return c;
     DraftArgs a;
     a.logits = logits;
     a.d2t = d2t;
@@ -294,11 +240,9 @@ sv_status spec_draft_sample(const void *logits, sv_dtype dtype, const int32_t *d
 
 sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma, uint64_t *counters,
                             hipStream_t stream) {
-    if (B < 0 || gamma < 0) return SV_ERR_INVALID_ARG;
-    if (gamma > SV_MAX_GAMMA) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!accept_len || !counters) return SV_ERR_INVALID_ARG;
-    if (!aligned(counters, sizeof(uint64_t))) return SV_ERR_INVALID_ARG;
+    bool go;
+    const sv_status c = check_count(accept_len, B, gamma, counters, &go);
+    if (!go) return c;
     return launch_count(accept_len, B, gamma, reinterpret_cast<unsigned long long *>(counters), stream) == hipSuccess
                ? SV_OK
                : SV_ERR_HIP;
@@ -307,13 +251,10 @@ sv_status spec_verify_count(const int32_t *accept_len, int32_t B, int32_t gamma,
 sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_len, const int32_t *cand,
                              const int32_t *branch_drafts, int32_t B, int32_t gamma, int32_t f, int32_t L,
                              int32_t *out_branch, int32_t *out_next, uint64_t *counters, hipStream_t stream) {
-    if (B < 0 || gamma < 0 || f < 1 || L < 0) return SV_ERR_INVALID_ARG;
-    if (gamma > SV_MAX_GAMMA || f > SV_MAX_FANOUT || L > SV_MAX_BRANCH_DRAFTS) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!out_tokens || !accept_len || !cand || !out_branch) return SV_ERR_INVALID_ARG;
-    if (out_next && L > 0 && !branch_drafts) return SV_ERR_INVALID_ARG;
-    if (counters && !aligned(counters, sizeof(uint64_t))) return SV_ERR_INVALID_ARG;
-    if (!grid_fits(((int64_t)B + 3) / 4)) return SV_ERR_TOO_LARGE;
+    bool go;
+    const sv_status c = check_fanout(out_tokens, accept_len, cand, branch_drafts, B, gamma, f, L, out_branch,
+                                     out_next, counters, &go);
+    if (!go) return c;
     FanoutArgs a;
     a.out_tokens = out_tokens;
     a.accept_len = accept_len;
@@ -329,20 +270,12 @@ sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_le
     return launch_fanout(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-size_t sv_workspace_bytes_vocab_trim(int32_t Vt) {
-    if (Vt < 1 || Vt > SV_MAX_VOCAB) return 0;
-    return workspace_need(trim_counter_bytes(Vt), trim_data_bytes(Vt));
-}
-
 sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P, int32_t *out_d2t,
                           int32_t *out_t2d, int32_t *out_vd, int64_t *out_info, void *workspace,
                           size_t workspace_bytes, hipStream_t stream) {
-    if (N < 0 || Vt < 1 || !(P > 0.0f)) return SV_ERR_INVALID_ARG;
-    if (Vt > SV_MAX_VOCAB || N > (int64_t)INT32_MAX) return SV_ERR_TOO_LARGE;
-    if ((N > 0 && !tokens) || !out_d2t || !out_vd || !workspace) return SV_ERR_INVALID_ARG;
-    if (out_info && !aligned(out_info, sizeof(int64_t))) return SV_ERR_INVALID_ARG;
-    const size_t cb = trim_counter_bytes(Vt);
-    if (!workspace_fits(workspace_bytes, cb, trim_data_bytes(Vt))) return SV_ERR_WORKSPACE_TOO_SMALL;
+    bool go;
+    const sv_status c = check_trim(tokens, N, Vt, P, out_d2t, out_vd, out_info, workspace, workspace_bytes, &go);
+    if (!go) return c;
     TrimArgs a;
     a.tokens = tokens;
     a.N = N;
@@ -357,79 +290,14 @@ sv_status spec_vocab_trim(const int32_t *tokens, int64_t N, int32_t Vt, float P,
     return launch_trim(a, stream) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
-size_t sv_workspace_bytes_lmhead(int32_t M, int32_t V) {
-    if (M < 0 || V < 1 || V > SV_MAX_VOCAB) return 0;
-    const size_t nt = ((size_t)V + kLmTile - 1) / kLmTile;
-    return workspace_need(256, align256(sizeof(uint64_t) * (size_t)M * nt) + align256(sizeof(ArgMax) * (size_t)M));
-}
-
-namespace {
-sv_status run_lmhead(const void *hidden, const void *W, const int32_t *tokens, const int32_t *parents, int32_t B,
-                     int32_t R, int32_t d, int32_t V, bool tree, int32_t *out_path, int32_t *out_tokens,
-                     int32_t *out_len, int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *ws,
-                     size_t ws_bytes, hipStream_t st) {
-    const int64_t M = (int64_t)B * R;
-    if (M > INT32_MAX) return SV_ERR_TOO_LARGE;
-    const size_t need = sv_workspace_bytes_lmhead((int32_t)M, V);
-    const size_t nt = ((size_t)V + kLmTile - 1) / kLmTile;
-    const size_t part_bytes = align256(sizeof(uint64_t) * (size_t)M * nt);
-    if (!workspace_fits(ws_bytes, 256, part_bytes + align256(sizeof(ArgMax) * (size_t)M))) return SV_ERR_WORKSPACE_TOO_SMALL;
-    (void)need;
-    LmheadArgs L;
-    L.hidden = static_cast<const uint16_t *>(hidden);
-    L.W = static_cast<const uint16_t *>(W);
-    L.M = (int32_t)M;
-    L.d = d;
-    L.V = V;
-    L.mtiles = (int32_t)((M + kLmTile - 1) / kLmTile);
-    L.ntiles = (int32_t)nt;
-    L.ntiles8 = (int32_t)(((nt + 1) / 2 + 7) / 8 * 8);
-    if (!grid_fits((int64_t)L.mtiles * L.ntiles8)) return SV_ERR_TOO_LARGE;
-    char *data = static_cast<char *>(ws) + counter_region(ws_bytes);
-    L.part = reinterpret_cast<uint64_t *>(data);
-    L.rowres = reinterpret_cast<ArgMax *>(data + part_bytes);
-    L.out_argmax = out_argmax;
-    L.out_maxlogit = out_maxlogit;
-    if (launch_lmhead(L, st) != hipSuccess) return SV_ERR_HIP;
-    GreedyArgs a;
-    a.logits = nullptr;
-    a.tokens = tokens;
-    a.parents = parents;
-    a.B = B;
-    a.rows_per_seq = R;
-    a.V = V;
-    a.chunks = 1;
-    a.tree = tree ? 1 : 0;
-    a.split_chunks = 0;
-    a.out_tokens = out_tokens;
-    a.out_len = out_len;
-    a.out_status = out_status;
-    a.out_path = out_path;
-    a.part = nullptr;
-    a.rowres = L.rowres;
-    a.counters = nullptr;
-    return launch_seq(a, st) == hipSuccess ? SV_OK : SV_ERR_HIP;
-}
-
-sv_status lmhead_check(const void *hidden, const void *W, int32_t B, int32_t R, int32_t d, int32_t V) {
-    if (B < 0 || R < 1 || d < 8 || V < 1) return SV_ERR_INVALID_ARG;
-    if (d % 8 != 0) return SV_ERR_INVALID_ARG;
-    if (V > SV_MAX_VOCAB) return SV_ERR_TOO_LARGE;
-    if (B == 0) return SV_OK;
-    if (!hidden || !W || !aligned(hidden, 16) || !aligned(W, 16)) return SV_ERR_INVALID_ARG;
-    return SV_OK;
-}
-}  // namespace
-
 sv_status spec_lmhead_verify_greedy(const void *hidden, const void *W, const int32_t *draft_tokens, int32_t B,
                                     int32_t gamma, int32_t d, int32_t V, int32_t *out_tokens, int32_t *out_accept_len,
                                     int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-    if (gamma < 0) return SV_ERR_INVALID_ARG;
-    if (gamma > SV_MAX_GAMMA) return SV_ERR_TOO_LARGE;
-    const sv_status c = lmhead_check(hidden, W, B, gamma + 1, d, V);
-    if (c != SV_OK || B == 0) return c;
-    if (!out_tokens || !out_accept_len || !workspace || (gamma > 0 && !draft_tokens)) return SV_ERR_INVALID_ARG;
+    bool go;
+    const sv_status c = check_lmhead(hidden, W, draft_tokens, nullptr, false, B, gamma + 1, d, V, nullptr, out_tokens,
+                                     out_accept_len, workspace, workspace_bytes, &go);
+    if (!go) return c;
     return run_lmhead(hidden, W, draft_tokens, nullptr, B, gamma + 1, d, V, false, nullptr, out_tokens,
                       out_accept_len, out_argmax, out_maxlogit, out_status, workspace, workspace_bytes, stream);
 }
@@ -439,11 +307,10 @@ sv_status spec_lmhead_verify_tree(const void *hidden, const void *W, const int32
                                   int32_t *out_path_nodes, int32_t *out_tokens, int32_t *out_accept_len,
                                   int32_t *out_argmax, float *out_maxlogit, int32_t *out_status, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-    if (N > SV_MAX_TREE_NODES) return SV_ERR_TOO_LARGE;
-    const sv_status c = lmhead_check(hidden, W, B, N, d, V);
-    if (c != SV_OK || B == 0) return c;
-    if (!node_tokens || !parents || !out_path_nodes || !out_tokens || !out_accept_len || !workspace)
-        return SV_ERR_INVALID_ARG;
+    bool go;
+    const sv_status c = check_lmhead(hidden, W, node_tokens, parents, true, B, N, d, V, out_path_nodes, out_tokens,
+                                     out_accept_len, workspace, workspace_bytes, &go);
+    if (!go) return c;
     return run_lmhead(hidden, W, node_tokens, parents, B, N, d, V, true, out_path_nodes, out_tokens, out_accept_len,
                       out_argmax, out_maxlogit, out_status, workspace, workspace_bytes, stream);
 }

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "spec_verify.h"
+#include "sv_host.h"
 
 namespace sv {
 
@@ -110,10 +111,6 @@ __device__ __forceinline__ T wave_max(T v) {
 }
 
 // Argmax pair: larger value wins; equal values go to the lower index.
-struct ArgMax {
-    float v;
-    int32_t i;
-};
 __device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
     return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
 }
@@ -129,10 +126,6 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
 }
 
 // Online softmax partial: s = sum over the elements of 2^((z - m) * c).
-struct MaxSum {
-    float m;
-    float s;
-};
 __device__ __forceinline__ MaxSum maxsum_merge(MaxSum a, MaxSum b, float c) {
     if (b.m > a.m) { MaxSum t = a; a = b; b = t; }
     if (b.m == -INFINITY) return a;            // also covers a.m == b.m == -inf

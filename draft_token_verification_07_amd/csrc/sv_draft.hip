@@ -41,9 +41,6 @@ namespace sv {
 
 constexpr int kDraftThreads = 512;
 constexpr int kDraftUnroll = 4;
-constexpr int kDraftMaxChunks = 8;
-constexpr int kDraftMinChunk = 8192;       // logits per chunk at least
-constexpr int kDraftTargetWgs = 256;       // chunks grow until the grid has about this many workgroups
 
 // Exact count select over a whole row (one workgroup): the key K* and tie
 // cut such that exactly K ids have key > K*, or key == K* and id <= tie cut
@@ -652,26 +649,6 @@ __global__ __launch_bounds__(NT) void count_kernel(const int32_t *len, int32_t B
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-int32_t draft_chunks(int32_t B, int32_t V) {
-    const int64_t want = ((int64_t)kDraftTargetWgs + (B > 0 ? B : 1) - 1) / (B > 0 ? B : 1);
-    int64_t cap = (int64_t)V / kDraftMinChunk;
-    if (cap < 1) cap = 1;
-    int64_t C = want < cap ? want : cap;
-    if (C > kDraftMaxChunks) C = kDraftMaxChunks;
-    if (C < 1) C = 1;
-    return (int32_t)C;
-}
-
-void draft_layout(int32_t B, int32_t V, DraftLayout *L, int32_t *C) {
-    const int32_t c = draft_chunks(B, V);
-    L->counter_bytes = align256(sizeof(uint32_t) * (size_t)B);
-    size_t off = 0;
-    L->res = off;   off = align256(off + sizeof(ChunkRes) * (size_t)B * c);
-    L->cand = off;  off = align256(off + (c > 1 ? sizeof(uint64_t) * (size_t)B * c * kCandCap : 0));
-    L->desc = off;  off = align256(off + sizeof(RowDesc) * (size_t)B);
-    L->data_bytes = off;
-    *C = c;
-}
 
 hipError_t launch_draft(const DraftArgs &a, int dtype, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)a.B * a.C));

@@ -273,25 +273,6 @@ static hipError_t launch_greedy_dt(const GreedyArgs &a, int grid, hipStream_t st
     return hipGetLastError();
 }
 
-bool greedy_split(int32_t R, int32_t C) { return R > kRowGroup || C > 1; }
-
-// Chunks per row.  Counted in 8-element vectors whatever the dtype, so the
-// workspace size depends on V and the row count only (a float32 chunk is
-// twice the bytes).  Rows are cut further, down to kGreedyMinChunkVecs
-// vectors, while the grid has fewer than kGreedyMinWgs workgroups.
-int32_t greedy_chunks(int32_t V, int64_t rows) {
-    const int64_t nvec = ((int64_t)V + 7) / 8;
-    const int64_t target = (int64_t)kGreedyThreads * kGreedyUnroll * kGreedyItersPerWg;
-    int64_t C = (nvec + target - 1) / target;
-    const int64_t want = (kGreedyMinWgs + rows - 1) / (rows > 0 ? rows : 1);
-    int64_t cap = nvec / kGreedyMinChunkVecs;
-    if (cap < 1) cap = 1;
-    const int64_t extra = want < cap ? want : cap;
-    if (extra > C) C = extra;
-    if (C < 1) C = 1;
-    if (C > kMaxChunks) C = kMaxChunks;
-    return (int32_t)C;
-}
 
 // The sequence step alone, on row results already in a.rowres (one per row,
 // published): the chain or the tree walk, one workgroup per sequence.

@@ -1921,63 +1921,6 @@ __global__ __launch_bounds__(NT) void pick_kernel(SampleArgs a) {
 // Host side: workspace layout and launches
 // ---------------------------------------------------------------------------
 
-// Chunks per row in plain mode: about 64 KiB of logits each, cut further
-// (down to kStatsMinChunk elements) while the grid has fewer than
-// kStatsMinWgs workgroups.  A function of the row length, element size and row
-// count only, so rows of equal length and type are cut the same way
-// (identical rows give identical statistics).
-static int32_t plain_chunks(int32_t V, int32_t ebytes, int64_t rows) {
-    const int64_t per = (int64_t)kStatsChunkBytes / ebytes;
-    int64_t C = ((int64_t)V + per - 1) / per;
-    const int64_t want = (kStatsMinWgs + rows - 1) / (rows > 0 ? rows : 1);
-    int64_t cap = (int64_t)V / kStatsMinChunk;
-    if (cap < 1) cap = 1;
-    const int64_t extra = want < cap ? want : cap;
-    if (extra > C) C = extra;
-    if (C < 1) C = 1;
-    if (C > kMaxChunks) C = kMaxChunks;
-    return (int32_t)C;
-}
-
-// Target ids per draw tile: kTile, halved (down to kTileMin) until the draw
-// has kDrawMinWgs workgroups.
-static int32_t draw_tile(int32_t B, int32_t Vt) {
-    int32_t tl = kTile;
-    while (tl > kTileMin && (int64_t)B * ((Vt + tl - 1) / tl) < kDrawMinWgs) tl >>= 1;
-    return tl;
-}
-
-// Kept-list slots per row: a row keeps at most as many ids as it has.
-int32_t kept_stride(int32_t Vt, int32_t Vd) {
-    const int32_t v = Vt > Vd ? Vt : Vd;
-    return v < kKeptCap ? v : kKeptCap;
-}
-
-bool sample_layout(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, int32_t bt, int32_t bd, bool topp,
-                   WorkspaceLayout *L, int32_t *Ct, int32_t *Cd, int32_t *tile, int32_t *ntiles) {
-    const size_t NR = (size_t)(2 * gamma + 1);
-    const int32_t ct = topp ? 1 : plain_chunks(Vt, bt, (int64_t)B * (int64_t)NR);
-    const int32_t cd = topp ? 1 : plain_chunks(Vd, bd, (int64_t)B * (int64_t)NR);
-    const int32_t tl = draw_tile(B, Vt);
-    const int32_t nt = (Vt + tl - 1) / tl;
-    L->cnt_stats = 0;
-    L->counter_bytes = align256(sizeof(uint32_t) * ((size_t)B + 1));     // arrival counters, then the map flag
-    size_t off = 0;
-    L->seq = off;       off = align256(off + sizeof(SeqState) * (size_t)B);
-    L->rows = off;      off = align256(off + sizeof(RowDesc) * (size_t)B * NR);
-    L->part = off;      off = align256(off + (topp ? 0 : sizeof(MaxSum) * (size_t)B * ((size_t)(gamma + 1) * ct + (size_t)gamma * cd)));
-    L->kept = off;      off = align256(off + (topp ? sizeof(KeptEnt) * (size_t)B * NR * kept_stride(Vt, Vd) : 0));
-    L->probe = off;     off = align256(off + (topp ? 0 : sizeof(Probe) * (size_t)B * (size_t)gamma));
-    L->tile_mass = off; off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt));
-    L->tile_sub = off;  off = align256(off + (topp ? 0 : sizeof(uint64_t) * (size_t)B * nt * kSubTiles));
-    L->tile_jb = off;   off = align256(off + (topp ? 0 : sizeof(int32_t) * ((size_t)nt + 1)));
-    L->data_bytes = off;
-    *Ct = ct;
-    *Cd = cd;
-    *tile = tl;
-    *ntiles = nt;
-    return true;
-}
 
 template <int DTT, int DTD>
 static hipError_t launch_sample_dt(const SampleArgs &a, hipStream_t st) {

@@ -562,79 +562,6 @@ __global__ __launch_bounds__(NT) void trim_write_kernel(TrimArgs a) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-namespace {
-struct TrimGeom {
-    int32_t R, logR, KB, S, nblocks;
-};
-TrimGeom trim_geom(int32_t Vt) {
-    TrimGeom g;
-    g.logR = 0;
-    while ((((int64_t)Vt + ((int64_t)1 << g.logR) - 1) >> g.logR) > kTrimBins) ++g.logR;
-    g.R = 1 << g.logR;
-    g.KB = (int32_t)(((((int64_t)Vt + g.R - 1) >> g.logR) + 3) & ~(int64_t)3);    // bins per range, padded to 4
-    int32_t s = kTrimTargetWgs / g.R;
-    if (s < 1) s = 1;
-    if (s > kTrimMaxSlices) s = kTrimMaxSlices;
-    g.S = s;
-    g.nblocks = (Vt + kTrimBlock - 1) / kTrimBlock;
-    return g;
-}
-struct TrimSizes {
-    size_t part, counts, hn, hm, h2, list, bd, st, total;
-};
-TrimSizes trim_sizes(int32_t Vt) {
-    const TrimGeom g = trim_geom(Vt);
-    TrimSizes z;
-    // S R <= max(kTrimTargetWgs, R) and KB <= min(kTrimBins, Vt): a bound
-    // that never shrinks as Vt grows, so a workspace sized for one vocabulary
-    // serves every smaller one
-    const size_t sr = (size_t)(g.R > kTrimTargetWgs ? g.R : kTrimTargetWgs);
-    const size_t kb = (size_t)(Vt < kTrimBins ? (Vt + 3) & ~3 : kTrimBins);
-    z.part = align256(sizeof(uint32_t) * sr * kb);
-    z.counts = align256(sizeof(uint32_t) * (size_t)Vt);
-    z.hn = align256(sizeof(uint32_t) * kTrimBuckets);
-    z.hm = align256(sizeof(unsigned long long) * kTrimBuckets);
-    z.h2 = align256(sizeof(uint32_t) * kTrimFine);
-    z.list = align256(sizeof(uint32_t) * kTrimList);
-    z.bd = align256(sizeof(uint32_t) * (size_t)g.nblocks);
-    z.st = align256(sizeof(TrimState));
-    z.total = z.part + z.counts + z.hn + z.hm + z.h2 + z.list + 2 * z.bd + z.st;
-    return z;
-}
-}  // namespace
-
-size_t trim_counter_bytes(int32_t Vt) { (void)Vt; return 256; }
-size_t trim_data_bytes(int32_t Vt) { return trim_sizes(Vt).total; }
-
-void trim_layout(TrimArgs &a, char *base, char *data) {
-    const TrimGeom g = trim_geom(a.Vt);
-    const TrimSizes z = trim_sizes(a.Vt);
-    a.R = g.R;
-    a.logR = g.logR;
-    a.KB = g.KB;
-    a.S = g.S;
-    a.nblocks = g.nblocks;
-    a.totals = reinterpret_cast<unsigned long long *>(base);
-    a.arrive = reinterpret_cast<uint32_t *>(base + 2 * sizeof(unsigned long long));
-    char *p = data;
-    a.part = reinterpret_cast<uint32_t *>(p);
-    p += z.part;
-    a.counts = reinterpret_cast<uint32_t *>(p);
-    p += z.counts;
-    a.hist_n = reinterpret_cast<uint32_t *>(p);
-    p += z.hn;
-    a.hist_m = reinterpret_cast<unsigned long long *>(p);
-    p += z.hm;
-    a.h2 = reinterpret_cast<uint32_t *>(p);
-    p += z.h2;
-    a.list = reinterpret_cast<uint32_t *>(p);
-    p += z.list;
-    a.blockdef = reinterpret_cast<uint32_t *>(p);
-    p += z.bd;
-    a.blocktie = reinterpret_cast<uint32_t *>(p);
-    p += z.bd;
-    a.state = reinterpret_cast<TrimState *>(p);
-}
 
 hipError_t launch_trim(const TrimArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((trim_part_kernel<kTrimPartThreads, kTrimPartUnroll>), dim3((unsigned)(a.R * a.S)),

@@ -48,7 +48,10 @@
 #define ORC_EMEM 2
 
 /* dtype codes of the raw logits: 0 = float32, 1 = bfloat16 bit patterns,
- * 2 = float64 (logits the oracle computed itself, e.g. from an lm_head). */
+ * 2 = float64 (logits the oracle computed itself, e.g. from an lm_head).
+ * Any other code is an argument error. */
+static int dtype_ok(int dtype) { return dtype == 0 || dtype == 1 || dtype == 2; }
+
 static double logit_at(const void *base, int dtype, size_t i)
 {
     if (dtype == 0) {
@@ -385,6 +388,7 @@ int oracle_verify_sample(const void *tl, int tdt, const void *dl, int ddt,
                          int nthreads)
 {
     if (B < 0 || gamma < 0 || Vt < 1 || Vd < 1 || !(T > 0.0) || !(rho > 0.0)) return ORC_EARG;
+    if (!dtype_ok(tdt) || (gamma > 0 && !dtype_ok(ddt))) return ORC_EARG;
     if (d2t == NULL && Vd != Vt) return ORC_EARG;
     if (B == 0) return ORC_OK;
     if (d2t && gamma > 0) {
@@ -448,7 +452,7 @@ int oracle_verify_sample(const void *tl, int tdt, const void *dl, int ddt,
 int oracle_row_dist(const void *z, int dtype, int V, double T, double rho, int top_k, int k_delta,
                     double *p, int32_t *k, double *margin_lo, double *margin_hi)
 {
-    if (V < 1 || !(T > 0.0) || !(rho > 0.0)) return -ORC_EARG;
+    if (V < 1 || !(T > 0.0) || !(rho > 0.0) || !dtype_ok(dtype)) return -ORC_EARG;
     yid_t *scr = malloc(sizeof(yid_t) * (size_t)V);
     if (!scr) return -ORC_EMEM;
     topp_info_t info;
@@ -536,7 +540,7 @@ int oracle_draft_sample(const void *logits, int dtype, const int32_t *d2t, const
                         int32_t *out_status, int32_t *out_flags, double *out_margin,
                         int32_t *out_k)
 {
-    if (B < 0 || V < 1 || !(T > 0.0) || !(rho > 0.0)) return ORC_EARG;
+    if (B < 0 || V < 1 || !(T > 0.0) || !(rho > 0.0) || !dtype_ok(dtype)) return ORC_EARG;
     double *p = malloc(sizeof(double) * (size_t)V);
     yid_t *scr = malloc(sizeof(yid_t) * (size_t)V);
     if (!p || !scr) { free(p); free(scr); return ORC_EMEM; }
@@ -753,7 +757,7 @@ int oracle_verify_greedy(const void *logits, int dtype, const int32_t *tokens,
                          int B, int gamma, int V, int32_t *out_tokens,
                          int32_t *out_len, int32_t *out_status)
 {
-    if (B < 0 || gamma < 0 || V < 1) return ORC_EARG;
+    if (B < 0 || gamma < 0 || V < 1 || !dtype_ok(dtype)) return ORC_EARG;
     for (int b = 0; b < B; ++b) {
         int32_t st = 0;
         int n = gamma;
@@ -850,7 +854,7 @@ int oracle_verify_tree_greedy(const void *logits, int dtype, const int32_t *node
                               int32_t *out_path, int32_t *out_tokens, int32_t *out_len,
                               int32_t *out_status)
 {
-    if (B < 0 || N < 1 || V < 1) return ORC_EARG;
+    if (B < 0 || N < 1 || V < 1 || !dtype_ok(dtype)) return ORC_EARG;
     int32_t *g = malloc(sizeof(int32_t) * (size_t)N);
     int32_t *depth = malloc(sizeof(int32_t) * (size_t)N);
     unsigned char *acc = malloc((size_t)N);
