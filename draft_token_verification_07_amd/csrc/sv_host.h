@@ -63,7 +63,10 @@ constexpr int kGreedyItersPerWg = SV_GREEDY_ITERS;
 constexpr int kGreedyMinWgs = SV_GREEDY_MIN_WGS;    // rows are cut until the grid has this many
 constexpr int kGreedyWideMaxWgs = 512;              // grids this small take SV_GREEDY_WIDE * kGreedyThreads per workgroup
 constexpr int kGreedyMinChunkVecs = 1024;           // ... but chunks keep this many 16-byte vectors
-constexpr int kRowGroup = 8;                        // longer sequences end the row launch and walk in a second
+#ifndef SV_ROW_GROUP
+#define SV_ROW_GROUP 8
+#endif
+constexpr int kRowGroup = SV_ROW_GROUP;             // longer sequences end the row launch and walk in a second
 constexpr int kStatsThreads = SV_STATS_THREADS;     // plain-mode row statistics
 constexpr int kStatsUnroll = SV_STATS_UNROLL;
 constexpr int kStatsItersPerWg = SV_STATS_ITERS;

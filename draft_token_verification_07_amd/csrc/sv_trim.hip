@@ -406,7 +406,7 @@ __device__ __forceinline__ void trim_cut(const TrimArgs &a, const TrimState &st)
         // from the top reaches T
         const int32_t L = min((int32_t)ld_agent_u32(&a.state->list_n), kTrimList);
         const int P = pow2_at_least(L > 1 ? L : 2);
-        for (int q = threadIdx.x; q < P; q += NT) s_l[q] = q < L ? (uint64_t)a.list[q] : 0ull;
+        for (int q = threadIdx.x; q < P; q += NT) s_l[q] = q < L ? (uint64_t)ld_agent_u32(&a.list[q]) : 0ull;
         bitonic_sort_u64<NT>(s_l, P);                          // ascending; ends with a barrier
         // the j-th largest is s_l[P - 1 - j]; thread i takes j in [PJ i, PJ (i + 1))
         const int PJ = (P + NT - 1) / NT;
@@ -466,8 +466,9 @@ __global__ __launch_bounds__(NT) void trim_refine_kernel(TrimArgs a) {
             wave_aggregate<false>(in, (int)(c - st.lo), 0ull,
                                   [&](int k, uint32_t n, uint64_t) { atomicAdd(&a.h2[k], n); });
         } else {
+            // published for the last workgroup, which may run on another XCD
             const int32_t pos = wave_append(in, reinterpret_cast<int32_t *>(&a.state->list_n));
-            if (in && pos < kTrimList) a.list[pos] = c;
+            if (in && pos < kTrimList) __hip_atomic_store(&a.list[pos], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (!arrive_last(&a.arrive[1], gridDim.x, &s_last)) return;
