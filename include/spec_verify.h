@@ -100,8 +100,10 @@ typedef enum {
 
 /*
  * Workspace sizes in bytes for a call with these sizes (0 only for invalid sizes).
- * The result depends only on the arguments, so a workspace sized for the
- * largest call serves every smaller one.
+ * The result depends only on the arguments and never decreases as any size
+ * argument grows (top_p held on the same side of 1), so a workspace sized for
+ * the largest call serves every smaller one.  The same holds for every other
+ * sv_workspace_bytes_*() below.
  */
 size_t sv_workspace_bytes_sample(int32_t B, int32_t gamma, int32_t Vt, int32_t Vd, float top_p);
 size_t sv_workspace_bytes_greedy(int32_t B, int32_t gamma, int32_t V);
