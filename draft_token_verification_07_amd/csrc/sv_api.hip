@@ -96,7 +96,7 @@ sv_status run_lmhead(const void *hidden, const void *W, const int32_t *tokens, c
     L.V = V;
     L.mtiles = (int32_t)((M + kLmTile - 1) / kLmTile);
     L.ntiles = (int32_t)nt;
-    L.ntiles8 = (int32_t)(((nt + 1) / 2 + 7) / 8 * 8);
+    L.ntiles8 = (int32_t)lmhead_col_tiles8(V);
     char *data = static_cast<char *>(ws) + counter_region(ws_bytes);
     L.part = reinterpret_cast<uint64_t *>(data);
     L.rowres = reinterpret_cast<ArgMax *>(data + lmhead_part_bytes(M, V));

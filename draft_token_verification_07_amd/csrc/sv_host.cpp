@@ -262,6 +262,12 @@ size_t lmhead_part_bytes(int64_t M, int32_t V) {
 size_t lmhead_data_bytes(int64_t M, int32_t V) {
     return lmhead_part_bytes(M, V) + align256(sizeof(ArgMax) * (size_t)M);
 }
+// GEMM column tiles (kLmGroup key tiles each), rounded up to a multiple of 8
+// so that the workgroups of one column tile share an XCD
+int64_t lmhead_col_tiles8(int32_t V) {
+    const int64_t nt = ((int64_t)V + kLmTile - 1) / kLmTile;
+    return ((nt + kLmGroup - 1) / kLmGroup + 7) / 8 * 8;
+}
 
 // ---------------------------------------------------------------------------
 // Argument checks
@@ -423,8 +429,7 @@ sv_status check_lmhead(const void *hidden, const void *W, const int32_t *tokens,
     if (M > INT32_MAX) return SV_ERR_TOO_LARGE;
     if (!workspace_fits(workspace_bytes, 256, lmhead_data_bytes(M, V))) return SV_ERR_WORKSPACE_TOO_SMALL;
     const int64_t mtiles = (M + kLmTile - 1) / kLmTile;
-    const int64_t nt = ((int64_t)V + kLmTile - 1) / kLmTile;
-    if (!grid_fits(mtiles * (((nt + 1) / 2 + 7) / 8 * 8))) return SV_ERR_TOO_LARGE;
+    if (!grid_fits(mtiles * lmhead_col_tiles8(V))) return SV_ERR_TOO_LARGE;
     *launch = true;
     return SV_OK;
 }

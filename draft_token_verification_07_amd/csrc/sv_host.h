@@ -130,13 +130,14 @@ struct LmheadArgs {
     const uint16_t *hidden;     // [M, d] bfloat16 bits, M = B * R
     const uint16_t *W;          // [V, d] bfloat16 bits
     int32_t M, d, V;
-    int32_t mtiles, ntiles, ntiles8;   // 128-row / 128-column tiles; ntiles8: 256-column GEMM tiles rounded up to 8
+    int32_t mtiles, ntiles, ntiles8;   // 128-row / 128-column tiles; ntiles8: GEMM column tiles rounded up to 8
     uint64_t *part;             // [M, ntiles] (value, ~id) max-keys per row and column tile
     ArgMax *rowres;             // [M] published row results
     int32_t *out_argmax;        // [M] or null
     float *out_maxlogit;        // [M] or null
 };
-constexpr int kLmTile = 128;
+constexpr int kLmTile = 128;      // rows per GEMM row tile, columns per key tile
+constexpr int kLmGroup = 4;       // key tiles per GEMM column tile (512 columns)
 
 // ---------------------------------------------------------------------------
 // Sampling
@@ -352,6 +353,7 @@ size_t greedy_ws(int32_t B, int32_t R, int32_t V);
 int64_t chunk_total_bound(int64_t rows, int64_t c0, int64_t cap, int64_t target, int64_t maxc);
 size_t lmhead_part_bytes(int64_t M, int32_t V);
 size_t lmhead_data_bytes(int64_t M, int32_t V);
+int64_t lmhead_col_tiles8(int32_t V);
 
 // Each check takes an entry point's arguments in the order its declaration
 // documents the failures.  It returns the call's status when the host

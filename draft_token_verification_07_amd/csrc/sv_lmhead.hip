@@ -12,20 +12,15 @@
 // logits[m][v] = sum_k hidden[m][k] * W[v][k], bfloat16 inputs, float32
 // accumulation on the matrix cores (v_mfma_f32_16x16x32_bf16: per lane, A
 // holds row l%16 and k 8(l/16)..+7, B column l%16 and the same k, and the
-// 16x16 result rows 4(l/16)..+3 of column l%16).  A workgroup of four waves
-// computes a 128 x 256 tile, each wave 64 x 128 (4 x 8 MFMA tiles), 32 k per
-// step.  Both matrices are k-contiguous: each step's operands are read as
-// coalesced 16-byte loads into registers while the matrix cores work on the
-// previous step, then written to the other half of a double-buffered LDS
-// stage (rows padded by 16 bytes), from which the waves take their MFMA
-// fragments.  The block order puts the row tiles that share
-// a weight tile on one XCD, so the weights are read from HBM about once.
+// 16x16 result rows 4(l/16)..+3 of column l%16).  Both matrices are
+// k-contiguous.  The block order puts the row tiles that share a weight tile
+// on one XCD, so the weights are read from HBM about once.
 //
-// Epilogue: per row and 128-column tile, the largest logit and its lowest id
-// as one 64-bit key (order-preserving key of the value, then ~id), stored
-// per tile.  lmhead_reduce_kernel takes the maximum key of each row and
-// publishes the row result, and the sequence step (chain or tree walk) of
-// the greedy path follows.
+// Epilogue: per row and 128-column key tile, the largest logit and its
+// lowest id as one 64-bit key (order-preserving key of the value, then ~id),
+// stored per tile.  lmhead_reduce_kernel takes the maximum key of each row
+// and publishes the row result, and the sequence step (chain or tree walk)
+// of the greedy path follows.
 #include "sv_common.h"
 #include "sv_internal.h"
 #include "sv_rows.h"
@@ -35,100 +30,159 @@ namespace sv {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kLmThreads = 256;
-constexpr int kLmBM = 128;                 // rows per workgroup tile
-constexpr int kLmBN = kLmTile * 2;         // columns per workgroup tile (two key tiles)
-constexpr int kLmBK = 32;                  // k per stage (one MFMA k)
-constexpr int kLmPitch = kLmBK * 2 + 16;   // LDS bytes per operand row (64 + 16 of padding)
+constexpr int kLmThreads = 128 * kLmGroup;      // 2 x kLmGroup waves, each a 64-row x 128-column tile
+constexpr int kLmBM = kLmTile;                  // rows per workgroup tile
+constexpr int kLmBN = kLmTile * kLmGroup;       // columns per workgroup tile: one key tile per wave column
+constexpr int kLmBK = 32;                       // k per stage (one MFMA k)
+constexpr int kLmPitch = kLmBK * 2;             // LDS bytes per operand row and stage
+constexpr int kLmPA = kLmBM * 4 / kLmThreads;   // 16-byte pieces of A per thread and stage
+constexpr int kLmPB = kLmBN * 4 / kLmThreads;   // 16-byte pieces of W per thread and stage
+static_assert(kLmThreads / kWave == 2 * kLmGroup, "2 x kLmGroup wave tiles");
 
-// One k-step of both operands in registers: A [kLmBM rows][64 B] and
-// B [kLmBN rows][64 B]; thread t holds the 16-byte pieces t, t + 256, ... of
-// the row-major [row][4 pieces] order (four threads per row, coalesced).
+// Position of 16-byte piece c of operand row r inside its 64-byte LDS row.
+// XOR-ing the piece index with ((r >> 1) ^ (r >> 3)) & 3 makes both access
+// patterns touch disjoint banks within any 8 or within any 16 consecutive
+// lanes (32 or 64 banks of 4 bytes): the stage writes (consecutive lanes
+// hold the four pieces of consecutive rows) and the fragment reads
+// (consecutive lanes hold one piece of consecutive rows).
+__device__ __forceinline__ int lm_piece(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
+
+// One stage (32 k) of both operands in registers: thread t holds the pieces
+// t, t + kLmThreads, ... of the row-major [row][4 pieces] order, so four
+// threads read each row's 64 contiguous bytes.
 struct Stage {
-    u32x4 a[kLmBM * 4 / kLmThreads];
-    u32x4 b[kLmBN * 4 / kLmThreads];
+    u32x4 a[kLmPA];
+    u32x4 b[kLmPB];
+    bool kin;     // this thread's pieces lie inside d (else they are stored as zeros)
 };
 
 __device__ __forceinline__ void stage_load(Stage &st, const uint16_t *A, const uint16_t *B, int32_t m0, int32_t n0,
                                            int32_t M, int32_t V, int32_t d, int32_t k0) {
+    // k past the end (a last stage shorter than 32, or a stage past d) reads
+    // the row's last piece and is stored as zeros: the loads themselves are
+    // unconditional and in bounds
+    const int32_t k = k0 + ((int)threadIdx.x % 4) * 8;
+    const int32_t kc = min(k, d - 8);
+    st.kin = k < d;
 #pragma unroll
-    for (int u = 0; u < kLmBM * 4 / kLmThreads; ++u) {
+    for (int u = 0; u < kLmPA; ++u) {
         const int p = u * kLmThreads + (int)threadIdx.x;
         const int32_t r = min(m0 + p / 4, M - 1);
-        const int32_t k = k0 + (p % 4) * 8;
-        st.a[u] = k < d ? *reinterpret_cast<const u32x4 *>(A + (size_t)r * d + k) : u32x4{0u, 0u, 0u, 0u};
+        st.a[u] = *reinterpret_cast<const u32x4 *>(A + (size_t)r * d + kc);
     }
 #pragma unroll
-    for (int u = 0; u < kLmBN * 4 / kLmThreads; ++u) {
+    for (int u = 0; u < kLmPB; ++u) {
         const int p = u * kLmThreads + (int)threadIdx.x;
         const int32_t c = min(n0 + p / 4, V - 1);
-        const int32_t k = k0 + (p % 4) * 8;
-        st.b[u] = k < d ? *reinterpret_cast<const u32x4 *>(B + (size_t)c * d + k) : u32x4{0u, 0u, 0u, 0u};
+        st.b[u] = *reinterpret_cast<const u32x4 *>(B + (size_t)c * d + kc);
     }
 }
 
 __device__ __forceinline__ void stage_store(const Stage &st, unsigned char *sa, unsigned char *sb) {
 #pragma unroll
-    for (int u = 0; u < kLmBM * 4 / kLmThreads; ++u) {
+    for (int u = 0; u < kLmPA; ++u) {
         const int p = u * kLmThreads + (int)threadIdx.x;
-        *reinterpret_cast<u32x4 *>(sa + (p / 4) * kLmPitch + (p % 4) * 16) = st.a[u];
+        *reinterpret_cast<u32x4 *>(sa + (p / 4) * kLmPitch + lm_piece(p / 4, p % 4) * 16) =
+            st.kin ? st.a[u] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < kLmBN * 4 / kLmThreads; ++u) {
+    for (int u = 0; u < kLmPB; ++u) {
         const int p = u * kLmThreads + (int)threadIdx.x;
-        *reinterpret_cast<u32x4 *>(sb + (p / 4) * kLmPitch + (p % 4) * 16) = st.b[u];
+        *reinterpret_cast<u32x4 *>(sb + (p / 4) * kLmPitch + lm_piece(p / 4, p % 4) * 16) =
+            st.kin ? st.b[u] : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
+__device__ __forceinline__ bf16x8 frag_a(const unsigned char *sa, int wm, int lr, int lg, int i) {
+    const int r = wm * 64 + 16 * i + lr;
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sa + r * kLmPitch + lm_piece(r, lg) * 16));
+}
+
+__device__ __forceinline__ bf16x8 frag_b(const unsigned char *sb, int wn, int lr, int lg, int j) {
+    const int r = wn * kLmTile + 16 * j + lr;
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sb + r * kLmPitch + lm_piece(r, lg) * 16));
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses only: global
+// loads of later stages stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A workgroup of eight waves (two per SIMD, one workgroup per CU) computes a
+// 128 x 512 tile of logits, each wave 64 x 128 (4 x 8 MFMA tiles, 128
+// accumulator registers).  The k loop is software-pipelined, one 32-k stage
+// per step:
+//  - the A operands of stage s + 1 are read from LDS at the start of step s
+//    and each W operand of stage s + 1 right after the MFMAs of its column,
+//    so the reads can overlap the matrix cores' work on stage s;
+//  - LDS holds stages s and s + 1 (two buffers of 40 KB); stage s + 2 is
+//    written to the buffer of stage s once every wave has read it;
+//  - the global loads of stage s + 3 are issued right after stage s + 2 is
+//    stored and stay in flight across the barrier, which waits for LDS
+//    accesses only.
 __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_kernel(LmheadArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char s_a[2][kLmBM * kLmPitch];
     __shared__ __attribute__((aligned(16))) unsigned char s_b[2][kLmBN * kLmPitch];
-    __shared__ uint64_t s_key[kLmBM][2];
     // block -> (row tile, column tile): the row tiles of one column tile on one XCD
     const int32_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
     const int32_t mt = slot % a.mtiles;
-    const int32_t nt2 = (slot / a.mtiles) * 8 + xcd;            // 256-column tile
-    if (nt2 * kLmBN >= a.V) return;
+    const int32_t ntg = (slot / a.mtiles) * 8 + xcd;            // column tile
+    if (ntg * kLmBN >= a.V) return;
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    const int wm = wv >> 1, wn = wv & 1;                         // wave tile: 64 rows x 128 columns
+    const int wm = wv / kLmGroup, wn = wv % kLmGroup;
     const int32_t M = a.M, V = a.V, d = a.d;
-    const int32_t bm0 = mt * kLmBM, bn0 = nt2 * kLmBN;
+    const int32_t bm0 = mt * kLmBM, bn0 = ntg * kLmBN;
     const int lr = lane & 15, lg = lane >> 4;
+    const int32_t nk = max(2, (d + kLmBK - 1) / kLmBK);   // 32-k stages; a stage past d reads as zeros
     f32x4 acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Stage st;
-    stage_load(st, a.hidden, a.W, bm0, bn0, M, V, d, 0);
-    stage_store(st, s_a[0], s_b[0]);
-    __syncthreads();
-    int buf = 0;
-    for (int32_t k0 = 0; k0 < d; k0 += kLmBK) {
-        const bool more = k0 + kLmBK < d;
-        if (more) stage_load(st, a.hidden, a.W, bm0, bn0, M, V, d, k0 + kLmBK);   // next stage, in flight
-        const unsigned char *sa = s_a[buf] + (wm * 64 + lr) * kLmPitch + lg * 16;
-        const unsigned char *sb = s_b[buf] + (wn * 128 + lr) * kLmPitch + lg * 16;
-        bf16x8 fa[4], fb[8];
+    // MFMA operands of the current stage: A rows wm * 64 + 16 i + (l % 16) and
+    // W rows (columns) wn * 128 + 16 j + (l % 16), k 8 (l / 16) .. + 7
+    bf16x8 fa[4], fb[8];
+    Stage s0;
+    stage_load(s0, a.hidden, a.W, bm0, bn0, M, V, d, 0);
+    stage_store(s0, s_a[0], s_b[0]);
+    stage_load(s0, a.hidden, a.W, bm0, bn0, M, V, d, kLmBK);
+    lds_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sa + i * 16 * kLmPitch));
+    for (int i = 0; i < 4; ++i) fa[i] = frag_a(s_a[0], wm, lr, lg, i);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sb + j * 16 * kLmPitch));
+    for (int j = 0; j < 8; ++j) fb[j] = frag_b(s_b[0], wn, lr, lg, j);
+    stage_store(s0, s_a[1], s_b[1]);
+    stage_load(s0, a.hidden, a.W, bm0, bn0, M, V, d, 2 * kLmBK);
+    lds_barrier();
+    for (int32_t k = 0; k < nk - 1; ++k) {
+        // stage k in fa and fb, stage k + 1 in LDS buffer nx, stage k + 2 in s0
+        const int nx = (k & 1) ^ 1;
+        bf16x8 na[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) na[i] = frag_a(s_a[nx], wm, lr, lg, i);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        if (more) {
-            // the buffer written here was last read before the previous barrier
-            stage_store(st, s_a[buf ^ 1], s_b[buf ^ 1]);
-            __syncthreads();
-            buf ^= 1;
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            fb[j] = frag_b(s_b[nx], wn, lr, lg, j);     // column j's MFMAs are issued: its next operand
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = na[i];
+        // every wave read stage k's buffer before the previous barrier
+        stage_store(s0, s_a[nx ^ 1], s_b[nx ^ 1]);
+        stage_load(s0, a.hidden, a.W, bm0, bn0, M, V, d, (k + 3) * kLmBK);   // may lie past d: zeros
+        lds_barrier();
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     // epilogue: per row, the largest logit over this wave's 128 columns (one
     // key tile), lowest id on ties -- per lane over its eight columns, then
-    // over the 16 lanes of the lane group holding the same rows
-    const int32_t n0 = bn0 + wn * 128;
+    // over the 16 lanes holding the same rows (MFMA result rows 4 (l / 16) + e
+    // of column l % 16)
+    const int32_t n0 = bn0 + wn * kLmTile;
+    const int32_t nt = ntg * kLmGroup + wn;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -146,15 +200,9 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                                        (uint32_t)__shfl_xor((int)(uint32_t)best, o, kWave);
                 best = other > best ? other : best;
             }
-            if (lr == 0) s_key[wm * 64 + 16 * i + lg * 4 + e][wn] = best;
+            const int32_t r = bm0 + wm * 64 + 16 * i + 4 * lg + e;
+            if (lr == 0 && r < M && nt < a.ntiles) a.part[(size_t)r * a.ntiles + nt] = best;
         }
-    }
-    __syncthreads();
-    {
-        const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;   // 256 threads: 128 rows x 2 key tiles
-        const int32_t r = bm0 + rr;
-        const int32_t nt = nt2 * 2 + half;
-        if (r < M && nt < a.ntiles) a.part[(size_t)r * a.ntiles + nt] = s_key[rr][half];
     }
 }
 
