@@ -491,13 +491,24 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def sources_sha() -> str:
-    """Hash of the kernel sources, so counter readings of an older kernel are
-    not reported for a changed one."""
+# Sources each workload's kernels are built from: its own kernel file(s) plus
+# the shared headers, host code and launch code.
+SHARED_SOURCES = ("sv_host.h", "sv_host.cpp", "sv_common.h", "sv_rows.h", "sv_internal.h", "sv_api.hip")
+KERNEL_SOURCES = {
+    "sample_topp": ("sv_sample.hip",), "sample_plain": ("sv_sample.hip",), "eagle_d2t": ("sv_sample.hip",),
+    "greedy": ("sv_greedy.hip",), "tree": ("sv_greedy.hip",), "draft": ("sv_draft.hip",),
+    "fanout": ("sv_fanout.hip",), "trim": ("sv_trim.hip",), "lmhead": ("sv_lmhead.hip", "sv_greedy.hip"),
+}
+
+
+def sources_sha(workload: str) -> str:
+    """Hash of the sources `workload`'s kernels are built from, so counter
+    readings of an older kernel are not reported for a changed one."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "draft_token_verification_07_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in sorted(SHARED_SOURCES + KERNEL_SOURCES[workload]):
+        h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -510,7 +521,7 @@ def read_traffic(path: str, workload: str):
         lines = open(path).read().splitlines()
     except OSError:
         return None
-    sha = sources_sha()
+    sha = sources_sha(workload)
     for ln in lines:
         cells = [c.strip() for c in ln.strip().strip("|").split("|")]
         if len(cells) >= 6 and cells[0] == workload and cells[1] == sha:
