@@ -41,10 +41,11 @@ static_assert(kLmThreads / kWave == 2 * kLmGroup, "2 x kLmGroup wave tiles");
 
 // Position of 16-byte piece c of operand row r inside its 64-byte LDS row.
 // XOR-ing the piece index with ((r >> 1) ^ (r >> 3)) & 3 makes both access
-// patterns touch disjoint banks within any 8 or within any 16 consecutive
-// lanes (32 or 64 banks of 4 bytes): the stage writes (consecutive lanes
-// hold the four pieces of consecutive rows) and the fragment reads
-// (consecutive lanes hold one piece of consecutive rows).
+// patterns touch disjoint banks within each aligned group of 8 lanes (32
+// banks of 4 bytes) and within each aligned group of 16 (64 banks): the stage
+// writes (consecutive lanes hold the four pieces of consecutive rows, rows
+// starting at multiples of 2 and 4) and the fragment reads (consecutive lanes
+// hold one piece of consecutive rows, starting at multiples of 16).
 __device__ __forceinline__ int lm_piece(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
 // One stage (32 k) of both operands in registers: thread t holds the pieces
