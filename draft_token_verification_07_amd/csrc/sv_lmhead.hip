@@ -207,6 +207,152 @@ __global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 }
 
+// ---------------------------------------------------------------------------
+// For d a multiple of 64: the same tiles with 64-k stages copied from global
+// memory straight into LDS (global_load_lds_dwordx4: lane i of a wave writes
+// 16 bytes at the wave's LDS address + 16 i).  A row segment of a stage is a
+// whole 128-byte line, a step carries 64 MFMAs per wave between barriers, and
+// no registers stage the data.  Two stages of 80 KB fill the LDS.
+// ---------------------------------------------------------------------------
+constexpr int kLmBK2 = 64;                                       // k per stage
+constexpr int kLmPitch2 = kLmBK2 * 2;                            // LDS bytes per operand row and stage
+constexpr int kLmStage2 = (kLmBM + kLmBN) * kLmPitch2;           // A rows, then W rows
+constexpr int kLmChunks2 = (kLmBM + kLmBN) / 8;                  // 1 KB chunks (8 rows) per stage
+constexpr int kLmChunksPerWave2 = kLmChunks2 / (kLmThreads / kWave);
+static_assert(kLmChunks2 % (kLmThreads / kWave) == 0, "whole chunks per wave");
+static_assert(2 * kLmStage2 <= 160 * 1024, "two stages fit the LDS");
+
+// Position of 16-byte piece c of row r inside its 128-byte LDS row: the XOR
+// with (r & 7) ^ ((r >> 3) & 1) keeps the fragment reads (consecutive lanes
+// hold one piece of consecutive rows) free of bank conflicts within each
+// aligned group of 8 lanes (32 banks) and of 16 lanes (64 banks).
+__device__ __forceinline__ int lm_piece8(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+
+// Stage k0 .. k0 + 63 of both operands into `sbuf`.  Chunk c covers stage rows
+// 8 c .. 8 c + 7 (A rows first); lane i fills physical piece i % 8 of row
+// i / 8, so it loads the logical piece the swizzle puts there.
+__device__ __forceinline__ void stage_dma64(unsigned char *sbuf, const uint16_t *A, const uint16_t *B, int32_t m0,
+                                            int32_t n0, int32_t M, int32_t V, int32_t d, int32_t k0, int wv,
+                                            int lane) {
+#pragma unroll
+    for (int q = 0; q < kLmChunksPerWave2; ++q) {
+        const int c = wv + q * (kLmThreads / kWave);
+        const bool isa = c < kLmBM / 8;                        // alike in the whole wave
+        const int r = (isa ? 8 * c : 8 * c - kLmBM) + lane / 8;     // row within A or within the W tile
+        const int piece = lm_piece8(r, lane % 8);
+        const uint16_t *src = isa ? A + (size_t)min(m0 + r, M - 1) * d : B + (size_t)min(n0 + r, V - 1) * d;
+        __builtin_amdgcn_global_load_lds(src + k0 + 8 * piece, sbuf + c * 1024, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bf16x8 frag_a64(const unsigned char *sa, int wm, int lr, int lg, int i, int h) {
+    const int r = wm * 64 + 16 * i + lr;
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4 *>(sa + r * kLmPitch2 + lm_piece8(r, 4 * h + lg) * 16));
+}
+__device__ __forceinline__ bf16x8 frag_b64(const unsigned char *sb, int wn, int lr, int lg, int j, int h) {
+    const int r = wn * kLmTile + 16 * j + lr;
+    return __builtin_bit_cast(bf16x8,
+                              *reinterpret_cast<const u32x4 *>(sb + r * kLmPitch2 + lm_piece8(r, 4 * h + lg) * 16));
+}
+
+__global__ __launch_bounds__(kLmThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_dma_kernel(
+    LmheadArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char s_st[2][kLmStage2];
+    const int32_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int32_t mt = slot % a.mtiles;
+    const int32_t ntg = (slot / a.mtiles) * 8 + xcd;            // column tile
+    if (ntg * kLmBN >= a.V) return;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const int wm = wv / kLmGroup, wn = wv % kLmGroup;
+    const int32_t M = a.M, V = a.V, d = a.d;
+    const int32_t bm0 = mt * kLmBM, bn0 = ntg * kLmBN;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int32_t nk = d / kLmBK2;                              // >= 1
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto dma = [&](int32_t s) {
+        stage_dma64(s_st[s & 1], a.hidden, a.W, bm0, bn0, M, V, d, s * kLmBK2, wv, lane);
+    };
+    dma(0);
+    if (nk > 1) {
+        dma(1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLmChunksPerWave2) : "memory");   // stage 0 landed (this wave)
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    lds_barrier();
+    bf16x8 fa[4], fb[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag_a64(s_st[0], wm, lr, lg, i, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb[j] = frag_b64(s_st[0] + kLmBM * kLmPitch2, wn, lr, lg, j, 0);
+    for (int32_t k = 0; k < nk; ++k) {
+        // stage k's first half in fa / fb; stage k + 1 in flight into the other
+        // buffer (issued here from k = 1 on: that buffer's stage k - 1 was read
+        // before the last barrier)
+        if (k >= 1 && k + 1 < nk) dma(k + 1);
+        const unsigned char *sa = s_st[k & 1];
+        const unsigned char *sb = sa + kLmBM * kLmPitch2;
+        // first half: its MFMAs, with the second half's operands read meanwhile
+        bf16x8 na[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) na[i] = frag_a64(sa, wm, lr, lg, i, 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            fb[j] = frag_b64(sb, wn, lr, lg, j, 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = na[i];
+        // second half
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        if (k + 1 < nk) {
+            // stage k + 1 landed (this wave's loads, then everyone's), then its first half
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            const unsigned char *na2 = s_st[(k + 1) & 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = frag_a64(na2, wm, lr, lg, i, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) fb[j] = frag_b64(na2 + kLmBM * kLmPitch2, wn, lr, lg, j, 0);
+        }
+    }
+    // epilogue as in lmhead_kernel
+    const int32_t n0 = bn0 + wn * kLmTile;
+    const int32_t nt = ntg * kLmGroup + wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int32_t c = n0 + 16 * j + lr;
+                const uint64_t key = c < V ? (((uint64_t)zkey(acc[i][j][e]) << 32) | (uint32_t)~(uint32_t)c) : 0ull;
+                best = key > best ? key : best;
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {
+                const uint64_t other = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), o, kWave) << 32) |
+                                       (uint32_t)__shfl_xor((int)(uint32_t)best, o, kWave);
+                best = other > best ? other : best;
+            }
+            const int32_t r = bm0 + wm * 64 + 16 * i + 4 * lg + e;
+            if (lr == 0 && r < M && nt < a.ntiles) a.part[(size_t)r * a.ntiles + nt] = best;
+        }
+    }
+}
+
 // One wave per row: the maximum key over the row's column tiles, published
 // as the row result (value, id); optionally written out.
 __global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmheadArgs a) {
@@ -234,7 +380,13 @@ __global__ __launch_bounds__(256) void lmhead_reduce_kernel(LmheadArgs a) {
 
 hipError_t launch_lmhead(const LmheadArgs &a, hipStream_t st) {
     const int64_t grid = (int64_t)a.mtiles * a.ntiles8;
-    hipLaunchKernelGGL(lmhead_kernel, dim3((unsigned)grid), dim3(kLmThreads), 0, st, a);
+#ifndef SV_LM_DMA
+#define SV_LM_DMA 1
+#endif
+    if (SV_LM_DMA && a.d % kLmBK2 == 0)
+        hipLaunchKernelGGL(lmhead_dma_kernel, dim3((unsigned)grid), dim3(kLmThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(lmhead_kernel, dim3((unsigned)grid), dim3(kLmThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_reduce_kernel, dim3((unsigned)((a.M + 3) / 4)), dim3(256), 0, st, a);
