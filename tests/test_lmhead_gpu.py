@@ -90,8 +90,10 @@ def _compare_chain(oracle_mod, w, seqs=None):
     return gpu
 
 
+# d a multiple of 64 takes the direct-to-LDS kernel (64-k stages), other d the
+# register-staged one (32-k stages, a partial last stage for d = 72 and 8)
 @pytest.mark.parametrize("B,R,d,V", [(2, 4, 64, 1000), (3, 7, 72, 5003), (1, 1, 8, 1), (5, 6, 256, 1283),
-                                     (7, 5, 512, 20000), (40, 7, 128, 3000)])
+                                     (7, 5, 512, 20000), (40, 7, 128, 3000), (1, 1, 64, 1), (3, 2, 192, 7)])
 def test_lmhead_chain_small(oracle_mod, B, R, d, V):
     _say("chain B=%d R=%d d=%d V=%d" % (B, R, d, V))
     _compare_chain(oracle_mod, synth.lmhead(9500 + d + V, B=B, R=R, d=d, V=V))
