@@ -253,7 +253,7 @@ KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
                tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel",
                trim="trim_part_kernel+trim_reduce_kernel+trim_select_kernel",
-               lmhead="lmhead_kernel+lmhead_reduce_kernel+seq_kernel")
+               lmhead="lmhead_dma_kernel+lmhead_reduce_kernel+seq_kernel")
 
 
 def measure(name, args, dev, log):
