@@ -9,11 +9,13 @@ the GPU, float64 in the oracle):
     - a sequence the oracle flags because a uniform lies within BAND of an
       accept threshold p/q or of an interior edge of the drawn token's CDF
       interval (an edge with another token of positive weight beyond it):
-      it is counted as a boundary sequence (the budget is 0.1 %);
+      it is counted as a boundary sequence;
     - a row whose top-p cumulative lands within BAND of top_p: the kept
       count one lower / higher is equally admissible, and the GPU must match
       the oracle run with one of those kept counts exactly (ints) and to the
       float tolerance.
+  Boundary and alternative sequences together stay within 0.1 % of the
+  batch (at least one), in every comparison.
 """
 from __future__ import annotations
 
@@ -118,6 +120,8 @@ def compare_sample(w, gpu, oracle_mod, nthreads=8, max_alt_rows=4):
                         gpu_p=gpu["p_tok"][b].tolist(), orc_p=orc["p_tok"][b].tolist(),
                         gpu_q=gpu["q_tok"][b].tolist(), orc_q=orc["q_tok"][b].tolist()))
     assert not bad, "%d sequences differ from the oracle: %s" % (len(bad), bad[:3])
+    assert boundary + alt <= max(1, int(0.001 * B)), \
+        "%d flagged boundary and %d alternative sequences of %d exceed the budget" % (boundary, alt, B)
     return dict(n=B, exact=exact, boundary=boundary, alternative=alt, oracle=orc)
 
 
