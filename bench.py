@@ -252,7 +252,7 @@ def cpu_baselines(w, max_seqs: int, work_seconds: float):
 KERNELS = dict(sample_topp="topp_kernel", sample_plain="stats_kernel+tile_kernel+pick_kernel",
                eagle_d2t="stats_kernel+tile_kernel+pick_kernel", greedy="greedy_kernel",
                tree="greedy_kernel+seq_kernel", draft="draft_kernel", fanout="fanout_kernel",
-               trim="trim_part_kernel+trim_reduce_kernel+trim_select_kernel",
+               trim="trim_part_kernel+trim_reduce_kernel+trim_refine_kernel+trim_count_kernel+trim_write_kernel",
                lmhead="lmhead_dma_kernel+lmhead_reduce_kernel+seq_kernel")
 
 

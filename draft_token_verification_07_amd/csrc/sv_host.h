@@ -293,7 +293,7 @@ struct TrimArgs {
     uint32_t *list;               // [kTrimList] counts inside the boundary bucket (wide buckets)
     uint32_t *blockdef, *blocktie;  // [nblocks] ids above the cut / on it, per block
     TrimState *state;
-    unsigned long long *totals;   // [2] valid, invalid (counter region; returned to zero)
+    unsigned long long *totals;   // [0]: valid tokens (counter region; returned to zero); [1] unused
     uint32_t *arrive;             // [2] arrival counters (counter region; returned to zero)
 };
 constexpr int kTrimBins = 32768;        // bins per partial-histogram workgroup (128 KiB of LDS)

@@ -19,7 +19,8 @@
 //     the partial histogram.  Ranges by residue spread the frequent ids of a
 //     skewed corpus over all ranges.  When S is a multiple of 8 the
 //     workgroups of one slice run on one XCD (the block order puts them S
-//     apart), so the slice is read from HBM once.  No global atomics.
+//     apart) and share its L2: the stream is fetched about 1.5 times instead
+//     of R times.  No global atomics.
 //   trim_reduce_kernel: sums the partial histograms of every id, and adds
 //     every id to a histogram of count buckets (exact below 128, then 64 per
 //     octave; count and mass).  The last workgroup finds the bucket holding
@@ -128,13 +129,10 @@ __device__ __forceinline__ uint32_t trim_take(double T, unsigned long long above
 // ---------------------------------------------------------------------------
 template <int NT, int U>
 __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
-    __shared__ uint32_t s_h[kTrimBins];
-    __shared__ uint32_t s_inv;
+    __shared__ uint32_t s_h[kTrimBins + 4];        // bin KB: the spare below
     const int32_t r = blockIdx.x / a.S, sl = blockIdx.x % a.S;
-    const int32_t Rm = a.R - 1, logR = a.logR;
-    const uint32_t Vt = (uint32_t)a.Vt;
-    for (int k = threadIdx.x; k < a.KB; k += NT) s_h[k] = 0;
-    if (threadIdx.x == 0) s_inv = 0;
+    const uint32_t Rm = (uint32_t)a.R - 1u, logR = (uint32_t)a.logR;
+    for (int k = threadIdx.x; k <= a.KB; k += NT) s_h[k] = 0;
     // what the later launches accumulate into starts at zero
     {
         const int32_t gsz = (int32_t)gridDim.x * NT, gi = (int32_t)blockIdx.x * NT + (int32_t)threadIdx.x;
@@ -145,12 +143,19 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
         for (int32_t k = gi; k < kTrimFine; k += gsz) a.h2[k] = 0;
     }
     __syncthreads();
-    uint32_t invalid = 0;
+    // Ids at or past KB R (negative ones too, as unsigned) are clamped to
+    // KB R, whose bin KB in range 0 is a spare that is never stored; ids in
+    // [Vt, KB R) land on bins of ids that do not exist, which the reduction
+    // skips.  So no token needs a range test of its own, and the invalid
+    // tokens are counted as N less the valid ones.
+    const uint32_t lim = (uint32_t)a.KB << logR;
+    auto cnt = [&](uint32_t t) {
+        const uint32_t u = min(t, lim);
+        if ((u & Rm) == (uint32_t)r) atomicAdd(&s_h[u >> logR], 1u);
+    };
     // ok: the token is real
     auto one = [&](int32_t t, bool ok) {
-        const bool inr = (uint32_t)t < Vt;
-        if (ok && inr && (t & Rm) == r) atomicAdd(&s_h[t >> logR], 1u);
-        if (r == 0 && ok && !inr) ++invalid;                  // counted once, by range 0
+        if (ok) cnt((uint32_t)t);
     };
     const uintptr_t base = reinterpret_cast<uintptr_t>(a.tokens);
     int64_t head = (int64_t)(((16u - (uint32_t)(base & 15u)) & 15u) / 4u);
@@ -166,8 +171,10 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
     const u32x4 *body = reinterpret_cast<const u32x4 *>(a.tokens + head);
     const int64_t v0 = nvec * sl / a.S, v1 = nvec * (sl + 1) / a.S;
     // rounds of U * NT vectors; the next round's loads are issued before
-    // this round's ids are counted (clamped indices past the slice)
+    // this round's ids are counted (clamped indices past the slice).  Full
+    // rounds count every id; the last, partial round checks its vectors.
     if (v1 > v0) {
+        constexpr int64_t step = (int64_t)U * NT;
         auto load = [&](int64_t vb, u32x4 (&raw)[U]) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -177,8 +184,21 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
         };
         u32x4 cur[U], nxt[U];
         load(v0, cur);
-        for (int64_t vb = v0; vb < v1; vb += (int64_t)U * NT) {
-            if (vb + (int64_t)U * NT < v1) load(vb + (int64_t)U * NT, nxt);
+        const int64_t nfull = (v1 - v0) / step;
+        int64_t vb = v0;
+        for (int64_t it = 0; it < nfull; ++it, vb += step) {
+            if (vb + step < v1) load(vb + step, nxt);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                cnt(cur[u].x);
+                cnt(cur[u].y);
+                cnt(cur[u].z);
+                cnt(cur[u].w);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+        if (vb < v1) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool ok = vb + (int64_t)u * NT + threadIdx.x < v1;
@@ -187,15 +207,11 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
                 one((int32_t)cur[u].z, ok);
                 one((int32_t)cur[u].w, ok);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
     }
-    if (r == 0 && invalid) atomicAdd(&s_inv, invalid);
     __syncthreads();
     uint32_t *dst = a.part + ((size_t)sl * a.R + r) * a.KB;
     for (int k = threadIdx.x; k < a.KB; k += NT) dst[k] = s_h[k];
-    if (r == 0 && threadIdx.x == 0 && s_inv) atomicAdd(&a.totals[1], (unsigned long long)s_inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -210,10 +226,10 @@ __device__ __forceinline__ void trim_boundary(const TrimArgs &a) {
     __shared__ unsigned long long s_aboveB;
     if (threadIdx.x == 0) {
         s_tot[0] = ld_agent_u64(&a.totals[0]);
-        s_tot[1] = ld_agent_u64(&a.totals[1]);
+        // every token is valid (an id in [0, Vt)) or invalid
+        s_tot[1] = (unsigned long long)a.N - s_tot[0];
         // the counter region goes back to zero (read by this workgroup only)
         __hip_atomic_store(&a.totals[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.totals[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_B = -1;
         s_aboveB = 0;
     }
