@@ -26,6 +26,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 1.2e-38 of the row maximum's.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier that waits for this wave's LDS accesses only: global
+// loads and atomics stay in flight across it (__syncthreads would wait for
+// them too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Element decoding.  bfloat16 widens to float32 exactly (it is the high half).
 // ---------------------------------------------------------------------------

@@ -187,7 +187,7 @@ TrimGeom trim_geom(int32_t Vt) {
     g.logR = 0;
     while ((((int64_t)Vt + ((int64_t)1 << g.logR) - 1) >> g.logR) > kTrimBins) ++g.logR;
     g.R = 1 << g.logR;
-    g.KB = (int32_t)(((((int64_t)Vt + g.R - 1) >> g.logR) + 3) & ~(int64_t)3);    // bins per range, padded to 4
+    g.KB = (int32_t)(((((int64_t)Vt + g.R - 1) >> g.logR) + 7) & ~(int64_t)7);    // bins per range, padded to 8
     int32_t s = kTrimTargetWgs / g.R;
     if (s < 1) s = 1;
     if (s > kTrimMaxSlices) s = kTrimMaxSlices;
@@ -201,12 +201,12 @@ struct TrimSizes {
 TrimSizes trim_sizes(int32_t Vt) {
     const TrimGeom g = trim_geom(Vt);
     TrimSizes z;
-    // S R <= max(kTrimTargetWgs, R) and KB <= min(kTrimBins, Vt): a bound
+    // S R <= max(kTrimTargetWgs, R) and KB <= min(kTrimBins, Vt rounded up to 8): a bound
     // that never shrinks as Vt grows, so a workspace sized for one vocabulary
     // serves every smaller one
     const size_t sr = (size_t)(g.R > kTrimTargetWgs ? g.R : kTrimTargetWgs);
-    const size_t kb = (size_t)(Vt < kTrimBins ? (Vt + 3) & ~3 : kTrimBins);
-    z.part = align256(sizeof(uint32_t) * sr * kb);
+    const size_t kb = (size_t)(Vt < kTrimBins ? (Vt + 7) & ~7 : kTrimBins);
+    z.part = align256(sizeof(uint16_t) * sr * kb);
     z.counts = align256(sizeof(uint32_t) * (size_t)Vt);
     z.hn = align256(sizeof(uint32_t) * kTrimBuckets);
     z.hm = align256(sizeof(unsigned long long) * kTrimBuckets);
@@ -219,7 +219,8 @@ TrimSizes trim_sizes(int32_t Vt) {
 }
 }  // namespace
 
-size_t trim_counter_bytes(int32_t Vt) { (void)Vt; return 256; }
+// totals and arrival counters, then the per-id overflow counts
+size_t trim_counter_bytes(int32_t Vt) { return 256 + align256(sizeof(uint32_t) * (size_t)Vt); }
 size_t trim_data_bytes(int32_t Vt) { return trim_sizes(Vt).total; }
 
 void trim_layout(TrimArgs &a, char *base, char *data) {
@@ -232,6 +233,7 @@ void trim_layout(TrimArgs &a, char *base, char *data) {
     a.nblocks = g.nblocks;
     a.totals = reinterpret_cast<unsigned long long *>(base);
     a.arrive = reinterpret_cast<uint32_t *>(base + 2 * sizeof(unsigned long long));
+    a.ovf = reinterpret_cast<uint32_t *>(base + 256);
     char *p = data;
     a.part = reinterpret_cast<uint32_t *>(p);
     p += z.part;

@@ -283,9 +283,10 @@ struct TrimArgs {
     int32_t *out_vd;              // [1]
     int64_t *out_info;            // [3] or null: kept mass, valid tokens, invalid tokens
     int32_t S;                    // stream slices
-    int32_t R, logR, KB;          // id ranges (ids t with t % R == r), bins per range (a multiple of 4)
+    int32_t R, logR, KB;          // id ranges (ids t with t % R == r), bins per range (a multiple of 8)
     int32_t nblocks;              // 1024-id blocks of the output pass
-    uint32_t *part;               // [S, R, KB] partial histograms
+    uint32_t *part;               // [S, R, KB / 2] partial histograms, two 16-bit bins per word
+    uint32_t *ovf;                // [Vt] counts moved out of 16-bit bins (counter region; returned to zero)
     uint32_t *counts;             // [Vt]
     uint32_t *hist_n;             // [kTrimBuckets] ids per count bucket
     unsigned long long *hist_m;   // [kTrimBuckets] their count sum
@@ -296,9 +297,9 @@ struct TrimArgs {
     unsigned long long *totals;   // [0]: valid tokens (counter region; returned to zero); [1] unused
     uint32_t *arrive;             // [2] arrival counters (counter region; returned to zero)
 };
-constexpr int kTrimBins = 32768;        // bins per partial-histogram workgroup (128 KiB of LDS)
+constexpr int kTrimBins = 65536;        // 16-bit bins per partial-histogram workgroup (128 KiB of LDS)
 constexpr int kTrimTargetWgs = 256;     // ranges x slices
-constexpr int kTrimMaxSlices = 64;
+constexpr int kTrimMaxSlices = 128;
 constexpr int kTrimBuckets = 1728;      // count buckets: exact below 128, then 64 per octave
 constexpr int kTrimFine = 4096;         // widest boundary bucket refined by an exact histogram
 constexpr int kTrimList = 4096;         // most ids in a wider boundary bucket

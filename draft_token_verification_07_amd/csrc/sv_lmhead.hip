@@ -104,10 +104,6 @@ __device__ __forceinline__ bf16x8 frag_b(const unsigned char *sb, int wn, int lr
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sb + r * kLmPitch + lm_piece(r, lg) * 16));
 }
 
-// Workgroup barrier that waits for this wave's LDS accesses only: global
-// loads of later stages stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // A workgroup of eight waves (two per SIMD, one workgroup per CU) computes a
 // 128 x 512 tile of logits, each wave 64 x 128 (4 x 8 MFMA tiles, 128
 // accumulator registers).  The k loop is software-pipelined, one 32-k stage

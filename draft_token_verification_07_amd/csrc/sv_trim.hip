@@ -14,17 +14,19 @@
 // of count >= c*) reaches T = P * valid.  Five launches, every one spread
 // over the chip; each launch boundary is the only synchronisation, except
 // where the last workgroup to arrive on a counter finishes a step:
-//   trim_part_kernel: workgroup (r, s) counts the ids t with t % R == r (an
-//     LDS histogram of ceil(Vt / R) bins) in slice s of the stream and stores
-//     the partial histogram.  Ranges by residue spread the frequent ids of a
-//     skewed corpus over all ranges.  When S is a multiple of 8 the
-//     workgroups of one slice run on one XCD (the block order puts them S
-//     apart) and share its L2: the stream is fetched about 1.5 times instead
-//     of R times.  No global atomics.
-//   trim_reduce_kernel: sums the partial histograms of every id, and adds
-//     every id to a histogram of count buckets (exact below 128, then 64 per
-//     octave; count and mass).  The last workgroup finds the bucket holding
-//     c*: the first from the top whose mass brings the total to T.
+//   trim_part_kernel: workgroup (r, s) counts the ids t with t % R == r in
+//     slice s of the stream (an LDS histogram of ceil(Vt / R) 16-bit bins,
+//     two per word; every few rounds the large bins move into per-id
+//     overflow counts) and stores the partial histogram.  Ranges by residue
+//     spread the frequent ids of a skewed corpus over all ranges.  When S is
+//     a multiple of 8 the workgroups of one slice run on one XCD (the block
+//     order puts them S apart) and share its L2.  Global atomics only for
+//     the rare overflow moves.
+//   trim_reduce_kernel: sums the partial histograms and the overflow count
+//     of every id (returning the latter to zero), and adds every id to a
+//     histogram of count buckets (exact below 128, then 64 per octave; count
+//     and mass).  The last workgroup finds the bucket holding c*: the first
+//     from the top whose mass brings the total to T.
 //   trim_refine_kernel: when that bucket spans several counts, the ids in it
 //     give an exact histogram of their counts (buckets up to kTrimFine wide)
 //     or a list of them (wider buckets hold counts >= 2^19, so at most
@@ -127,12 +129,26 @@ __device__ __forceinline__ uint32_t trim_take(double T, unsigned long long above
 // ---------------------------------------------------------------------------
 // Launch 1: partial histograms
 // ---------------------------------------------------------------------------
+// Bins are 16-bit counters, two to a word (bin k in the low half of word
+// k / 2 when k is even), so a range holds twice the ids a 32-bit bin would
+// and each token is examined by half as many workgroups.  No bin can wrap:
+// every three rounds a sweep moves each bin of kTrimSpill or more into the
+// id's overflow count (a global atomic, rare: only ids holding an eighth of
+// a segment get there), and a segment between sweeps adds at most three
+// rounds (plus a few unaligned tokens) to a bin.
+constexpr uint32_t kTrimSpill = 0x2000u;
+constexpr int kTrimSweepRounds = 3;
+static_assert((kTrimSpill - 1) + (uint32_t)kTrimSweepRounds * kTrimPartUnroll * kTrimPartThreads * 4 + 8 <= 0xffffu,
+              "a 16-bit bin cannot wrap between sweeps");
+
 template <int NT, int U>
 __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
-    __shared__ uint32_t s_h[kTrimBins + 4];        // bin KB: the spare below
+    static_assert(NT == kTrimPartThreads && U == kTrimPartUnroll, "the sweep bound assumes this round size");
+    __shared__ uint32_t s_h[kTrimBins / 2 + 4];    // bin KB (low half of word KB / 2): the spare below
     const int32_t r = blockIdx.x / a.S, sl = blockIdx.x % a.S;
     const uint32_t Rm = (uint32_t)a.R - 1u, logR = (uint32_t)a.logR;
-    for (int k = threadIdx.x; k <= a.KB; k += NT) s_h[k] = 0;
+    const int32_t words = a.KB >> 1;               // KB is a multiple of 8
+    for (int k = threadIdx.x; k <= words; k += NT) s_h[k] = 0;
     // what the later launches accumulate into starts at zero
     {
         const int32_t gsz = (int32_t)gridDim.x * NT, gi = (int32_t)blockIdx.x * NT + (int32_t)threadIdx.x;
@@ -149,9 +165,37 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
     // skips.  So no token needs a range test of its own, and the invalid
     // tokens are counted as N less the valid ones.
     const uint32_t lim = (uint32_t)a.KB << logR;
+    const uint32_t wsh = logR + 1u;                // id -> word
     auto cnt = [&](uint32_t t) {
         const uint32_t u = min(t, lim);
-        if ((u & Rm) == (uint32_t)r) atomicAdd(&s_h[u >> logR], 1u);
+        if ((u & Rm) == (uint32_t)r) {
+            // bin u >> logR: word u >> (logR + 1), half (u >> logR) & 1
+            const uint32_t half = __builtin_amdgcn_ubfe(u, logR, 1u);
+            atomicAdd(&s_h[u >> wsh], half * 0xffffu + 1u);
+        }
+    };
+    // Moves every bin of kTrimSpill or more into its id's overflow count
+    // (bins of ids past Vt are just cleared).  Called by the whole workgroup.
+    const uint32_t Vt = (uint32_t)a.Vt;
+    auto sweep = [&]() {
+        lds_barrier();
+        for (int k = threadIdx.x; k <= words; k += NT) {
+            const uint32_t w = s_h[k];
+            if (w & 0xe000e000u) {
+                uint32_t f0 = w & 0xffffu, f1 = w >> 16;
+                const uint32_t t0 = ((uint32_t)(2 * k) << logR) + (uint32_t)r, t1 = t0 + (1u << logR);
+                if (f0 >= kTrimSpill) {
+                    if (t0 < Vt) atomicAdd(&a.ovf[t0], f0);
+                    f0 = 0;
+                }
+                if (f1 >= kTrimSpill) {
+                    if (t1 < Vt) atomicAdd(&a.ovf[t1], f1);
+                    f1 = 0;
+                }
+                s_h[k] = f0 | (f1 << 16);
+            }
+        }
+        lds_barrier();
     };
     // ok: the token is real
     auto one = [&](int32_t t, bool ok) {
@@ -197,6 +241,7 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            if ((it + 1) % kTrimSweepRounds == 0 && vb + step < v1) sweep();
         }
         if (vb < v1) {
 #pragma unroll
@@ -210,8 +255,8 @@ __global__ __launch_bounds__(NT) void trim_part_kernel(TrimArgs a) {
         }
     }
     __syncthreads();
-    uint32_t *dst = a.part + ((size_t)sl * a.R + r) * a.KB;
-    for (int k = threadIdx.x; k < a.KB; k += NT) dst[k] = s_h[k];
+    uint32_t *dst = a.part + ((size_t)sl * a.R + r) * words;
+    for (int k = threadIdx.x; k < words; k += NT) dst[k] = s_h[k];
 }
 
 // ---------------------------------------------------------------------------
@@ -312,30 +357,31 @@ __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
         s_hm[b] = 0;
     }
     __syncthreads();
-    // thread: bins k0..k0+3 of range r (one 16-byte load per slice; rows of
-    // KB bins, KB a multiple of 4), i.e. ids (k0 + q) R + r
+    // thread: bins k0..k0+3 of range r (one 8-byte load of two words per
+    // slice, kTrimRedBatch slices in flight; rows of KB / 2 words, KB a
+    // multiple of 8), i.e. ids (k0 + q) R + r, plus their overflow counts
+    constexpr int kTrimRedBatch = 16;
     const int32_t i = (int32_t)blockIdx.x * NT + (int32_t)threadIdx.x;      // over [0, R * KB / 4)
     const int32_t q4 = a.KB >> 2;
     const int32_t r = i / q4, k0 = (i - r * q4) << 2;
     const bool own = r < a.R;
     u32x4 c4 = {0u, 0u, 0u, 0u};
     if (own) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.part + (size_t)r * a.KB + k0);
-        const size_t stride = ((size_t)a.R * a.KB) >> 2;
+        const int32_t words = a.KB >> 1;
+        const uint2 *p = reinterpret_cast<const uint2 *>(a.part + (size_t)r * words + (k0 >> 1));
+        const size_t stride = ((size_t)a.R * words) >> 1;
+        auto add = [&](const uint2 &w) {
+            c4.x += w.x & 0xffffu; c4.y += w.x >> 16; c4.z += w.y & 0xffffu; c4.w += w.y >> 16;
+        };
         int32_t sl = 0;
-        for (; sl + 16 <= a.S; sl += 16) {
-            u32x4 q[16];
+        for (; sl + kTrimRedBatch <= a.S; sl += kTrimRedBatch) {
+            uint2 q[kTrimRedBatch];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) q[u] = p[(size_t)(sl + u) * stride];
+            for (int u = 0; u < kTrimRedBatch; ++u) q[u] = p[(size_t)(sl + u) * stride];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                c4.x += q[u].x; c4.y += q[u].y; c4.z += q[u].z; c4.w += q[u].w;
-            }
+            for (int u = 0; u < kTrimRedBatch; ++u) add(q[u]);
         }
-        for (; sl < a.S; ++sl) {
-            const u32x4 q = p[(size_t)sl * stride];
-            c4.x += q.x; c4.y += q.y; c4.z += q.z; c4.w += q.w;
-        }
+        for (; sl < a.S; ++sl) add(p[(size_t)sl * stride]);
     }
     // the workgroup's bucket histogram in LDS, then one global add per
     // nonzero bucket (a bucket of small counts holds most ids of a skewed
@@ -344,8 +390,14 @@ __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int32_t t = ((k0 + q) << a.logR) + r;
-        const uint32_t c = q == 0 ? c4.x : q == 1 ? c4.y : q == 2 ? c4.z : c4.w;
+        uint32_t c = q == 0 ? c4.x : q == 1 ? c4.y : q == 2 ? c4.z : c4.w;
         if (own && t < a.Vt) {
+            // the overflow count goes back to zero for the next call
+            const uint32_t o = a.ovf[t];
+            if (o) {
+                c += o;
+                a.ovf[t] = 0;
+            }
             a.counts[t] = c;
             csum += c;
             if (c > 0) {

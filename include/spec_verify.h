@@ -291,7 +291,8 @@ sv_status spec_fanout_lookup(const int32_t *out_tokens, const int32_t *accept_le
  *   out_vd     [1] int32: the number of kept ids (device memory).
  *   out_info   [3] int64 or NULL: kept count mass, valid tokens, invalid tokens.
  *   workspace  >= sv_workspace_bytes_vocab_trim(Vt) bytes, zeroed once when
- *              allocated (its totals are returned to zero by every call).
+ *              allocated (its totals and per-id overflow counts are returned
+ *              to zero by every call).
  * Errors: SV_ERR_INVALID_ARG (N < 0, Vt < 1, P <= 0 or NaN, null required
  * pointers), SV_ERR_TOO_LARGE (Vt > SV_MAX_VOCAB or N > INT32_MAX),
  * SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP.

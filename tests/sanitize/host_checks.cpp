@@ -163,11 +163,16 @@ static void trim() {
             const char *c = static_cast<const char *>(p);
             return c >= data && c + bytes <= base + need;
         };
-        EXPECT(a.R >= 1 && (a.R & (a.R - 1)) == 0 && a.KB % 4 == 0 && a.KB <= kTrimBins);
+        EXPECT(a.R >= 1 && (a.R & (a.R - 1)) == 0 && a.KB % 8 == 0 && a.KB <= kTrimBins);
         EXPECT((int64_t)a.R * a.KB >= Vt);
-        EXPECT(inside(a.part, sizeof(uint32_t) * (size_t)a.S * a.R * a.KB));
-        EXPECT(reinterpret_cast<char *>(a.part) + sizeof(uint32_t) * (size_t)a.S * a.R * a.KB <=
+        // 16-bit bins, two per word
+        EXPECT(inside(a.part, sizeof(uint16_t) * (size_t)a.S * a.R * a.KB));
+        EXPECT(reinterpret_cast<char *>(a.part) + sizeof(uint16_t) * (size_t)a.S * a.R * a.KB <=
                reinterpret_cast<char *>(a.counts));
+        // the overflow counts sit in the counter region, after the totals and arrival counters
+        EXPECT(reinterpret_cast<char *>(a.ovf) >= reinterpret_cast<char *>(a.arrive) + 2 * sizeof(uint32_t));
+        EXPECT(reinterpret_cast<char *>(a.ovf) + sizeof(uint32_t) * (size_t)Vt <= base + trim_counter_bytes(Vt));
+        EXPECT(base + trim_counter_bytes(Vt) <= data);
         EXPECT(inside(a.counts, sizeof(uint32_t) * (size_t)Vt));
         EXPECT(inside(a.hist_n, sizeof(uint32_t) * kTrimBuckets));
         EXPECT(inside(a.hist_m, sizeof(unsigned long long) * kTrimBuckets));

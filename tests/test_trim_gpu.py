@@ -147,3 +147,28 @@ def test_trim_ids_outside_the_vocabulary(oracle_mod, Vt):
     for P in (0.95, 1.0):
         o = _check(oracle_mod, tok, Vt, P)
         assert o[2][2] == 300 * len(edge)
+
+
+def test_trim_dominant_ids_overflow_16bit_bins(oracle_mod):
+    """Ids holding most of the stream push their 16-bit LDS bins past the
+    spill threshold many times per workgroup; their counts come back exactly
+    through the overflow counts, which every call returns to zero."""
+    import torch
+    import draft_token_verification_07_amd as sv
+    rng = np.random.default_rng(9430)
+    Vt = 128256
+    need = sv.sv_workspace_bytes_vocab_trim(Vt)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    N = 3_000_000
+    tok = rng.integers(0, Vt, N).astype(np.int32)
+    pick = rng.random(N)
+    tok[pick < 0.60] = 7
+    tok[(pick >= 0.60) & (pick < 0.85)] = Vt - 1
+    tok[(pick >= 0.85) & (pick < 0.86)] = -5
+    for P in (0.5, 0.9, 0.95):
+        _check(oracle_mod, tok, Vt, P, ws=ws)
+    _check(oracle_mod, np.full(1 << 21, 4242, np.int32), Vt, 0.95, ws=ws)
+    _check(oracle_mod, np.full(70000, 0, np.int32), 1, 0.95, ws=ws)
+    torch.cuda.synchronize()
+    K = (need // 8) & ~255                          # the counter region of this workspace size
+    assert int(ws[:K].sum().item()) == 0
