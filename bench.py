@@ -381,7 +381,7 @@ def measure(name, args, dev, log):
                rows_per_step=rows, bytes_per_step=nbytes, rotated_input_copies=nrot,
                ms_per_step=ms_per_step, rows_per_s=rows * K / (total_ms / 1e3),
                seqs_per_s=float(_batch(w) * K / (total_ms / 1e3)),
-               achieved_GBps=achieved, frac=achieved / PEAK_GBS,
+               achieved_GBps=achieved, bound="hbm", frac=achieved / PEAK_GBS,
                traffic=read_traffic(args.traffic_table, name),
                launch_ms_mean=float(np.mean(per_launch_ms)), launch_ms_median=float(np.median(per_launch_ms)),
                launch_ms_p10=float(np.percentile(per_launch_ms, 10)),
@@ -390,7 +390,10 @@ def measure(name, args, dev, log):
         B, R, d = w["hidden"].shape
         flops = 2.0 * B * R * w["W"].shape[0] * d
         tf = flops / (ms_per_step / 1e3) / 1e12
-        res.update(bound="mfma", flops_per_step=flops, achieved_TFLOPs=tf, mfma_frac=tf / PEAK_BF16_TFLOPS)
+        # frac is against the peak of the bound (the bf16 MFMA peak); the HBM
+        # rate of the same step is kept beside it
+        res.update(bound="mfma", flops_per_step=flops, achieved_TFLOPs=tf, mfma_frac=tf / PEAK_BF16_TFLOPS,
+                   frac=tf / PEAK_BF16_TFLOPS, hbm_frac=achieved / PEAK_GBS)
         log("[bench] %s: %.2f us/step, %.0f TFLOP/s (%.3f of the bf16 MFMA peak), %.0f GB/s"
             % (name, ms_per_step * 1e3, tf, tf / PEAK_BF16_TFLOPS, achieved))
     else:
