@@ -429,36 +429,41 @@ __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
 // ---------------------------------------------------------------------------
 // Launch 3: the exact cut inside the boundary bucket
 // ---------------------------------------------------------------------------
+// The fields it needs are read from the state one by one (uniform loads):
+// a copy of the whole struct is kept in per-thread memory by the compiler.
 template <int NT>
-__device__ __forceinline__ void trim_cut(const TrimArgs &a, const TrimState &st) {
+__device__ __forceinline__ void trim_cut(const TrimArgs &a) {
     __shared__ uint64_t s_tmp[NT / kWave];
     __shared__ uint32_t s_cs;
     __shared__ unsigned long long s_above;
     __shared__ uint64_t s_l[kTrimList];
-    const double T = st.T;
+    const TrimState *sp = a.state;
+    const double T = sp->T;
+    const unsigned long long aboveB = sp->aboveB;
+    const uint32_t lo = sp->lo, hi = sp->hi;
     if (threadIdx.x == 0) {
         s_cs = 0;
-        s_above = st.aboveB;
+        s_above = aboveB;
     }
     __syncthreads();
-    if (st.refine == 1) {
+    if (sp->refine == 1) {
         // exact histogram over [lo, hi]: thread i takes the values
         // (hi - PER (i + 1), hi - PER i]
         constexpr int PER = (kTrimFine + NT - 1) / NT;
-        const int64_t top = (int64_t)st.hi - (int64_t)PER * threadIdx.x;
+        const int64_t top = (int64_t)hi - (int64_t)PER * threadIdx.x;
         uint64_t m = 0;
         for (int q = 0; q < PER; ++q) {
             const int64_t v = top - q;
-            if (v >= (int64_t)st.lo) m += (uint64_t)v * ld_agent_u32(&a.h2[v - st.lo]);
+            if (v >= (int64_t)lo) m += (uint64_t)v * ld_agent_u32(&a.h2[v - lo]);
         }
         uint64_t all;
-        const uint64_t before = st.aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
+        const uint64_t before = aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
         if ((double)before < T && (double)(before + m) >= T) {
             unsigned long long acc = before;
             for (int q = 0; q < PER; ++q) {
                 const int64_t v = top - q;
-                if (v < (int64_t)st.lo) break;
-                const unsigned long long mv = (unsigned long long)v * ld_agent_u32(&a.h2[v - st.lo]);
+                if (v < (int64_t)lo) break;
+                const unsigned long long mv = (unsigned long long)v * ld_agent_u32(&a.h2[v - lo]);
                 if (mv == 0) continue;
                 if ((double)(acc + mv) >= T) {
                     s_cs = (uint32_t)v;
@@ -484,7 +489,7 @@ __device__ __forceinline__ void trim_cut(const TrimArgs &a, const TrimState &st)
             if (j < P) m += s_l[P - 1 - j];
         }
         uint64_t all;
-        const uint64_t before = st.aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
+        const uint64_t before = aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
         if ((double)before < T && (double)(before + m) >= T) {
             unsigned long long acc = before;
             for (int q = 0; q < PJ; ++q) {
@@ -506,32 +511,35 @@ __device__ __forceinline__ void trim_cut(const TrimArgs &a, const TrimState &st)
             if (s_l[q] > cs) mg += s_l[q];
         uint64_t g;
         (void)wg_excl_scan_u64<NT>(mg, s_tmp, &g);
-        if (threadIdx.x == 0) s_above = st.aboveB + g;
+        if (threadIdx.x == 0) s_above = aboveB + g;
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        TrimState o = st;
-        const uint32_t cs = s_cs > 0 ? s_cs : st.lo;          // found by construction
-        o.cstar = cs;
-        o.above = s_above;
-        o.take = trim_take(T, o.above, cs);
-        *a.state = o;
+        const uint32_t cs = s_cs > 0 ? s_cs : lo;             // found by construction
+        const unsigned long long above = s_above;
+        a.state->cstar = cs;
+        a.state->above = above;
+        a.state->take = trim_take(T, above, cs);
     }
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void trim_refine_kernel(TrimArgs a) {
     __shared__ int s_last;
-    const TrimState st = *a.state;
-    if (st.mode != 2 || st.refine == 0) return;               // alike in every workgroup: none arrives
+    // Alike in every workgroup (none then arrives).  The fields are read on
+    // their own, as uniform loads: a copy of the whole state per thread cost
+    // ~7 us even for the common cut that needs no refining.
+    const int32_t refine = a.state->refine;
+    if (a.state->mode != 2 || refine == 0) return;
+    const uint32_t lo = a.state->lo, hi = a.state->hi;
     const int32_t t0 = ((int32_t)blockIdx.x * NT + (int32_t)threadIdx.x) * 4;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int32_t t = t0 + u;
         const uint32_t c = t < a.Vt ? a.counts[t] : 0u;
-        const bool in = c >= st.lo && c <= st.hi && c > 0;
-        if (st.refine == 1) {
-            wave_aggregate<false>(in, (int)(c - st.lo), 0ull,
+        const bool in = c >= lo && c <= hi && c > 0;
+        if (refine == 1) {
+            wave_aggregate<false>(in, (int)(c - lo), 0ull,
                                   [&](int k, uint32_t n, uint64_t) { atomicAdd(&a.h2[k], n); });
         } else {
             // published for the last workgroup, which may run on another XCD
@@ -540,7 +548,7 @@ __global__ __launch_bounds__(NT) void trim_refine_kernel(TrimArgs a) {
         }
     }
     if (!arrive_last(&a.arrive[1], gridDim.x, &s_last)) return;
-    trim_cut<NT>(a, st);
+    trim_cut<NT>(a);
 }
 
 // ---------------------------------------------------------------------------
