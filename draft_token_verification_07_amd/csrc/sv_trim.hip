@@ -366,6 +366,13 @@ __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
     const int32_t r = i / q4, k0 = (i - r * q4) << 2;
     const bool own = r < a.R;
     u32x4 c4 = {0u, 0u, 0u, 0u};
+    // the ids' overflow counts, loaded first so that their latency hides
+    // under the slices' loads
+    // (unconditional loads at clamped ids, used only for ids this thread
+    // owns: a load under a divergent branch is waited for inside it)
+    uint32_t ov[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ov[q] = a.ovf[min(max(((k0 + q) << a.logR) + r, 0), a.Vt - 1)];
     if (own) {
         const int32_t words = a.KB >> 1;
         const uint2 *p = reinterpret_cast<const uint2 *>(a.part + (size_t)r * words + (k0 >> 1));
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(NT) void trim_reduce_kernel(TrimArgs a) {
         uint32_t c = q == 0 ? c4.x : q == 1 ? c4.y : q == 2 ? c4.z : c4.w;
         if (own && t < a.Vt) {
             // the overflow count goes back to zero for the next call
-            const uint32_t o = a.ovf[t];
+            const uint32_t o = ov[q];
             if (o) {
                 c += o;
                 a.ovf[t] = 0;
