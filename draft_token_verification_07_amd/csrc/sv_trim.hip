@@ -284,29 +284,33 @@ __device__ __forceinline__ void trim_boundary(const TrimArgs &a) {
     const int mode = valid == 0 ? 0 : (T >= (double)valid ? 1 : 2);
     if (mode == 2) {
         // thread i takes buckets [top - PER (i + 1), top - PER i): chunk sums,
-        // the mass above each chunk, then the crossing chunk walks its buckets
+        // the mass above each chunk, then the crossing chunk walks its buckets.
+        // The masses are loaded in one round (unconditionally, at clamped
+        // indices) and kept for the walk.
         const int hiB = kTrimBuckets - 1 - PER * (int)threadIdx.x;
+        unsigned long long mb[PER];
         uint64_t m = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int b = hiB - q;
-            if (b >= 0) m += ld_agent_u64(&a.hist_m[b]);
+            const unsigned long long v = ld_agent_u64(&a.hist_m[max(hiB - q, 0)]);
+            mb[q] = hiB - q >= 0 ? v : 0ull;
+            m += mb[q];
         }
         uint64_t all;
         const uint64_t before = wg_excl_scan_u64<NT>(m, s_tmp, &all);
         if ((double)before < T && (double)(before + m) >= T) {
             unsigned long long acc = before;
+            bool found = false;
+#pragma unroll
             for (int q = 0; q < PER; ++q) {
-                const int b = hiB - q;
-                if (b < 0) break;
-                const unsigned long long mb = ld_agent_u64(&a.hist_m[b]);
-                if (mb == 0) continue;
-                if ((double)(acc + mb) >= T) {
-                    s_B = b;
+                if (found || hiB - q < 0 || mb[q] == 0) continue;
+                if ((double)(acc + mb[q]) >= T) {
+                    s_B = hiB - q;
                     s_aboveB = acc;
-                    break;
+                    found = true;
+                } else {
+                    acc += mb[q];
                 }
-                acc += mb;
             }
         }
         __syncthreads();
