@@ -462,26 +462,32 @@ __device__ __forceinline__ void trim_cut(const TrimArgs &a) {
         // (hi - PER (i + 1), hi - PER i]
         constexpr int PER = (kTrimFine + NT - 1) / NT;
         const int64_t top = (int64_t)hi - (int64_t)PER * threadIdx.x;
+        // the masses v * (ids of count v), loaded in one round (clamped
+        // indices) and kept for the walk
+        unsigned long long mv[PER];
         uint64_t m = 0;
+#pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int64_t v = top - q;
-            if (v >= (int64_t)lo) m += (uint64_t)v * ld_agent_u32(&a.h2[v - lo]);
+            const uint32_t n = ld_agent_u32(&a.h2[v >= (int64_t)lo ? v - lo : 0]);
+            mv[q] = v >= (int64_t)lo ? (unsigned long long)v * n : 0ull;
+            m += mv[q];
         }
         uint64_t all;
         const uint64_t before = aboveB + wg_excl_scan_u64<NT>(m, s_tmp, &all);
         if ((double)before < T && (double)(before + m) >= T) {
             unsigned long long acc = before;
+            bool found = false;
+#pragma unroll
             for (int q = 0; q < PER; ++q) {
-                const int64_t v = top - q;
-                if (v < (int64_t)lo) break;
-                const unsigned long long mv = (unsigned long long)v * ld_agent_u32(&a.h2[v - lo]);
-                if (mv == 0) continue;
-                if ((double)(acc + mv) >= T) {
-                    s_cs = (uint32_t)v;
+                if (found || mv[q] == 0) continue;
+                if ((double)(acc + mv[q]) >= T) {
+                    s_cs = (uint32_t)(top - q);
                     s_above = acc;
-                    break;
+                    found = true;
+                } else {
+                    acc += mv[q];
                 }
-                acc += mv;
             }
         }
         __syncthreads();
