@@ -172,3 +172,13 @@ def test_trim_dominant_ids_overflow_16bit_bins(oracle_mod):
     torch.cuda.synchronize()
     K = (need // 8) & ~255                          # the counter region of this workspace size
     assert int(ws[:K].sum().item()) == 0
+
+
+def test_trim_full_size(oracle_mod):
+    """The benchmarked workload itself: 2^24 Zipf(1.1) tokens over Vt=128256,
+    P=0.95, from the generator and seed the benchmark uses (two residue ranges
+    of 16-bit bins, 128 slices)."""
+    w = synth.WORKLOADS["trim"](2002)
+    assert w["tokens"].shape[0] == 1 << 24 and w["Vt"] == 128256
+    o = _check(oracle_mod, w["tokens"], w["Vt"], w["P"])
+    _say("full size: kept %d ids, mass %d of %d valid" % (len(o[0]), o[2][0], o[2][1]))
