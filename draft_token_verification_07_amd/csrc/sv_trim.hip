@@ -133,8 +133,8 @@ __device__ __forceinline__ uint32_t trim_take(double T, unsigned long long above
 // k / 2 when k is even), so a range holds twice the ids a 32-bit bin would
 // and each token is examined by half as many workgroups.  No bin can wrap:
 // every three rounds a sweep moves each bin of kTrimSpill or more into the
-// id's overflow count (a global atomic, rare: only ids holding an eighth of
-// a segment get there), and a segment between sweeps adds at most three
+// id's overflow count (a global atomic, rare: only ids holding about a sixth
+// of a segment get there), and a segment between sweeps adds at most three
 // rounds (plus a few unaligned tokens) to a bin.
 constexpr uint32_t kTrimSpill = 0x2000u;
 constexpr int kTrimSweepRounds = 3;
