@@ -11,7 +11,7 @@ import pytest
 
 from draft_token_verification_07_amd import synth
 
-from helpers import assert_same, compare_sample, run_greedy, run_sample, run_tree
+from helpers import assert_same, compare_sample, run_greedy, run_sample, run_tree, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -311,15 +311,29 @@ def test_sample_status_bits(oracle_mod):
 
 
 def test_workspace_shared_across_entry_points_and_sizes(oracle_mod):
-    """One zeroed workspace, sized for the largest call, serves greedy, tree
-    and sampling calls of different batch sizes in any order (the counters
-    sit below a bound that depends on the workspace size alone)."""
+    """One zeroed workspace, sized for the largest call, serves greedy, tree,
+    sampling and vocabulary-trim calls of different sizes in any order (the
+    counters sit below a bound that depends on the workspace size alone, and
+    every call returns them to zero; the trim's include per-id overflow
+    counts, exercised by a dominant id)."""
     import torch
     import draft_token_verification_07_amd as sv
     need = max(sv.sv_workspace_bytes_sample(40, 5, 30011, 30011, 0.9), sv.sv_workspace_bytes_sample(40, 5, 30011, 30011, 1.0),
-               sv.sv_workspace_bytes_greedy(40, 6, 30011), sv.sv_workspace_bytes_tree(40, 32, 30011))
+               sv.sv_workspace_bytes_greedy(40, 6, 30011), sv.sv_workspace_bytes_tree(40, 32, 30011),
+               sv.sv_workspace_bytes_vocab_trim(30011))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(930)
+    tok = rng.integers(0, 30011, 10_000_000).astype(np.int32)
+    tok[rng.random(tok.shape[0]) < 0.6] = 5                # bins past the spill threshold in every slice
+    trim_ref = oracle_mod.vocab_trim(tok, 30011, 0.95)
+    tok_dev = to_dev(tok)
     for rep in range(2):
+        d2t, t2d, vd, info = sv.spec_vocab_trim(tok_dev, 30011, 0.95, ws=ws)
+        torch.cuda.synchronize()
+        n = int(vd.item())
+        np.testing.assert_array_equal(d2t.cpu().numpy()[:n], trim_ref[0])
+        np.testing.assert_array_equal(t2d.cpu().numpy(), trim_ref[1])
+        np.testing.assert_array_equal(info.cpu().numpy(), trim_ref[2])
         for B in (40, 3, 17):
             g = synth.greedy(900 + B, B=B, gamma=6, V=30011)
             assert_same(run_greedy(g, ws=ws), oracle_mod.verify_greedy(g["target"], g["tokens"]),
@@ -331,6 +345,9 @@ def test_workspace_shared_across_entry_points_and_sizes(oracle_mod):
                 w = synth.sample_topp(920 + B, B=B, gamma=5, V=30011)
                 w["top_p"] = top_p
                 compare_sample(w, run_sample(w, ws=ws), oracle_mod)
+    torch.cuda.synchronize()
+    K = (need // 8) & ~255                          # the counter region of this workspace size
+    assert int(ws[:K].sum().item()) == 0
 
 
 def test_sample_reproducible_and_workspace_reuse(oracle_mod):
