@@ -130,16 +130,18 @@ def test_trim_large_vocab_and_one_id(oracle_mod):
     _check(oracle_mod, np.array([0, 3, 3, -7], np.int32), 1, 0.5)
 
 
-@pytest.mark.parametrize("Vt", [4099, 65537, 131073, 128256, 1])
+@pytest.mark.parametrize("Vt", [4099, 65537, 131073, 128256, 1, 65536, 131072])
 def test_trim_ids_outside_the_vocabulary(oracle_mod, Vt):
     """Ids just past Vt (inside the padding of the last histogram row), far
-    past it and negative ones, at vocabularies of 1, 4 and 8 residue ranges:
-    none is counted as an id, all are counted as invalid."""
+    past it and negative ones, at vocabularies of 1, 2, 4 and 8 residue
+    ranges, and at the two sizes whose bins fill the LDS histogram exactly
+    (the spare bin then sits in its last word): none is counted as an id,
+    all are counted as invalid."""
     rng = np.random.default_rng(9420 + Vt % 97)
     R = 1
-    while -(-Vt // R) > 32768:
+    while -(-Vt // R) > 65536:
         R *= 2
-    KB = (-(-Vt // R) + 3) & ~3
+    KB = (-(-Vt // R) + 7) & ~7
     edge = np.array([Vt, Vt + 1, KB * R - 1, KB * R, KB * R + 1, 2 ** 31 - 1, -1, -2 ** 31, -R], np.int64)
     edge = edge[(edge >= -2 ** 31) & (edge < 2 ** 31) & ((edge < 0) | (edge >= Vt))].astype(np.int32)
     good = rng.integers(0, Vt, 50000).astype(np.int32)
